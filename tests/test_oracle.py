@@ -1,0 +1,413 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+No GPU.  Every oracle function is pinned here by something other than itself:
+hand-derived worked examples, closed forms, special cases, invariants of the
+softmax, brute force in scalar Python, and a library routine (torch's CPU
+float64 scaled_dot_product_attention).  test_oracle_mutants.py checks that
+plausible planted mistakes fail at least one of these pins.
+
+Page references:
+  SA  = «Самовнимание, ядра CUDA и FlashAttention» (section 1: Scores and
+        Attention equations, rows of the softmax sum to one; section 3: tiling
+        and the online softmax).
+  FA  = «Flash Attention» skill page (quick start; scenario 1, step 4: the
+        explicit softmax(q@k^T/8)@v check; scenario 2, step 3: MQA/GQA and the
+        (left, right) sliding window).
+  NEWS = the-ai.news article, section «Внимание типа FlashAttention и
+        постраничное внимание» (paged KV cache: block table, paging does not
+        change the logical elements).
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import CONFIGS, dense_inputs, paged_inputs, random_dense
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+TIGHT = 1e-12
+
+MASKS = [(False, -1), (True, -1), (False, 3), (True, 3), (True, 0), (False, 0)]
+
+
+def rnd(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def small_case(B=2, Hq=4, Hkv=2, Lq=9, Lk=13, D=8, seed=0):
+    r = np.random.default_rng(seed)
+    q = r.standard_normal((B, Lq, Hq, D))
+    k = r.standard_normal((B, Lk, Hkv, D))
+    v = r.standard_normal((B, Lk, Hkv, D))
+    return q, k, v
+
+
+# ---------------------------------------------------------------- golden
+
+def test_golden_worked_examples():
+    """Hand-derived examples (SA section 1; bottom-right causal; window; GQA)."""
+    with open(os.path.join(HERE, "golden", "worked_examples.json")) as f:
+        data = json.load(f)
+    for c in data["cases"]:
+        out, lse = oracle.attention(np.array(c["q"]), np.array(c["k"]), np.array(c["v"]),
+                                    c["scale"], c["causal"], c["window"])
+        np.testing.assert_allclose(out, np.array(c["out"]), atol=data["tolerance"], rtol=0, err_msg=c["name"])
+        np.testing.assert_allclose(lse, np.array(c["lse"]), atol=data["tolerance"], rtol=0, err_msg=c["name"])
+
+
+# ---------------------------------------------------------------- P1
+
+def test_p1_probability_rows_sum_to_one():
+    """SA section 1: the row softmax turns scores into probabilities summing to 1."""
+    S = rnd((40, 57), 1) * 7
+    ok = np.random.default_rng(2).random((40, 57)) < 0.3
+    ok[np.arange(40), np.arange(40)] = True
+    P, lse = oracle.row_softmax(S, ok)
+    assert np.all(P[~ok] == 0)
+    np.testing.assert_allclose(P.sum(1), 1.0, atol=TIGHT, rtol=0)
+    # lse is the log of the sum of exponentials of the allowed entries
+    ref = np.array([math.log(sum(math.exp(S[i, j]) for j in range(57) if ok[i, j])) for i in range(40)])
+    np.testing.assert_allclose(lse, ref, atol=1e-12, rtol=0)
+
+
+@pytest.mark.parametrize("causal,window", MASKS)
+def test_p1_ones_value_gives_ones(causal, window):
+    """Rows summing to one means V = 1 gives out = 1 on every non-empty row."""
+    q, k, _ = small_case(seed=3)
+    v = np.ones_like(k)
+    out, lse = oracle.attention(q, k, v, 0.37, causal, window)
+    np.testing.assert_allclose(out, 1.0, atol=TIGHT, rtol=0)
+    assert np.all(np.isfinite(lse))
+
+
+# ---------------------------------------------------------------- P2
+
+@pytest.mark.parametrize("causal,window", MASKS)
+def test_p2_identical_keys_average_visible_values(causal, window):
+    """Identical keys give equal weights, so each row is the plain mean of the
+    values it may see, and lse = score + ln(count)."""
+    B, Hq, Hkv, Lq, Lk, D = 1, 2, 1, 7, 11, 3
+    q = rnd((B, Lq, Hq, D), 4)
+    k = np.broadcast_to(rnd((1, 1, Hkv, D), 5), (B, Lk, Hkv, D)).copy()
+    v = rnd((B, Lk, Hkv, D), 6)
+    out, lse = oracle.attention(q, k, v, 0.5, causal, window)
+    off = Lk - Lq
+    for i in range(Lq):
+        lo, hi = 0, Lk - 1
+        if causal:
+            hi = min(hi, i + off)
+        if window >= 0:
+            lo = max(lo, i + off - window)
+            if not causal:
+                hi = min(hi, i + off + window)
+        cnt = hi - lo + 1
+        for h in range(Hq):
+            np.testing.assert_allclose(out[0, i, h], v[0, lo:hi + 1, 0].mean(0), atol=TIGHT, rtol=0)
+            s = 0.5 * float(np.dot(q[0, i, h], k[0, 0, 0]))
+            assert abs(lse[0, h, i] - (s + math.log(cnt))) < 1e-12
+
+
+# ---------------------------------------------------------------- P3
+
+def test_p3_causal_row0_and_window0():
+    q, k, v = small_case(Lq=10, Lk=10, seed=7)
+    out, _ = oracle.attention(q, k, v, 0.3, causal=True)
+    for h in range(4):
+        assert np.array_equal(out[:, 0, h], v[:, 0, h // 2])  # row 0 sees only key 0: exact
+    out0, lse0 = oracle.attention(q, k, v, 0.3, causal=True, window=0)
+    for h in range(4):
+        assert np.array_equal(out0[:, :, h], v[:, :, h // 2])  # W = 0: each row sees only itself
+        s = float(np.float32(0.3)) * np.einsum("bid,bid->bi", q[:, :, h], k[:, :, h // 2])
+        np.testing.assert_allclose(lse0[:, h], s, atol=TIGHT, rtol=0)
+
+
+def test_p3_bottom_right_alignment_is_suffix_of_square():
+    """Causal with Lq < Lk equals the last Lq rows of the square causal problem."""
+    q, k, v = small_case(Lq=13, Lk=13, seed=8)
+    full, lfull = oracle.attention(q, k, v, 0.4, causal=True, window=4)
+    part, lpart = oracle.attention(q[:, 8:], k, v, 0.4, causal=True, window=4)
+    np.testing.assert_allclose(part, full[:, 8:], atol=TIGHT, rtol=0)
+    np.testing.assert_allclose(lpart, lfull[:, :, 8:], atol=TIGHT, rtol=0)
+
+
+def test_p3_empty_rows():
+    """Lq > Lk under causal alignment leaves the first Lq-Lk rows with no key."""
+    q, k, v = small_case(Lq=9, Lk=4, seed=9)
+    out, lse = oracle.attention(q, k, v, 0.4, causal=True)
+    assert np.all(out[:, :5] == 0) and np.all(np.isneginf(lse[:, :, :5]))
+    assert np.all(np.isfinite(lse[:, :, 5:]))
+
+
+# ---------------------------------------------------------------- P4
+
+def test_p4_closed_form_two_keys():
+    """Lk = 2: out = v0 + sigmoid(s1 - s0) (v1 - v0), lse = logaddexp(s0, s1)."""
+    r = np.random.default_rng(10)
+    for _ in range(20):
+        D = int(r.integers(1, 9))
+        q = r.standard_normal((1, 1, 1, D)) * 2
+        k = r.standard_normal((1, 2, 1, D)) * 2
+        v = r.standard_normal((1, 2, 1, D))
+        sc = float(np.float32(r.random() + 0.1))
+        out, lse = oracle.attention(q, k, v, sc)
+        s0 = sc * sum(q[0, 0, 0, d] * k[0, 0, 0, d] for d in range(D))
+        s1 = sc * sum(q[0, 0, 0, d] * k[0, 1, 0, d] for d in range(D))
+        sig = 1.0 / (1.0 + math.exp(-(s1 - s0)))
+        np.testing.assert_allclose(out[0, 0, 0], v[0, 0, 0] + sig * (v[0, 1, 0] - v[0, 0, 0]), atol=1e-12, rtol=0)
+        assert abs(lse[0, 0, 0] - np.logaddexp(s0, s1)) < 1e-12
+
+
+def _brute(q, k, v, sc, causal, window):
+    """Scalar Python attention: one query, one head at a time."""
+    B, Lq, Hq, D = q.shape
+    Lk, Hkv = k.shape[1], k.shape[2]
+    out = np.zeros_like(q, shape=(B, Lq, Hq, D))
+    lse = np.full((B, Hq, Lq), -math.inf)
+    for b, i, h in itertools.product(range(B), range(Lq), range(Hq)):
+        g = h * Hkv // Hq
+        vis = []
+        for j in range(Lk):
+            diag = i + Lk - Lq
+            if causal and j > diag:
+                continue
+            if window >= 0 and (j < diag - window or (not causal and j > diag + window)):
+                continue
+            vis.append(j)
+        if not vis:
+            continue
+        s = {j: sc * sum(float(q[b, i, h, d]) * float(k[b, j, g, d]) for d in range(D)) for j in vis}
+        mx = max(s.values())
+        w = {j: math.exp(s[j] - mx) for j in vis}
+        tot = sum(w.values())
+        for d in range(D):
+            out[b, i, h, d] = sum(w[j] * float(v[b, j, g, d]) for j in vis) / tot
+        lse[b, h, i] = mx + math.log(tot)
+    return out, lse
+
+
+@pytest.mark.parametrize("causal,window", MASKS + [(False, 1), (True, 5)])
+@pytest.mark.parametrize("Lq,Lk", [(1, 1), (5, 5), (3, 8), (8, 3), (7, 6)])
+def test_p4_brute_force_tiny(causal, window, Lq, Lk):
+    q, k, v = small_case(B=2, Hq=4, Hkv=2, Lq=Lq, Lk=Lk, D=4, seed=Lq * 31 + Lk)
+    out, lse = oracle.attention(q, k, v, 0.45, causal, window)
+    bo, bl = _brute(q, k, v, float(np.float32(0.45)), causal, window)
+    np.testing.assert_allclose(out, bo, atol=1e-12, rtol=0)
+    np.testing.assert_array_equal(np.isneginf(lse), np.isneginf(bl))
+    fin = np.isfinite(bl)
+    np.testing.assert_allclose(lse[fin], bl[fin], atol=1e-12, rtol=0)
+
+
+# ---------------------------------------------------------------- P5 / P6
+
+@pytest.mark.parametrize("causal,window", MASKS)
+@pytest.mark.parametrize("block", [1, 5, 16, 64])
+def test_p5_online_softmax_equals_full(causal, window, block):
+    """SA section 3: block-by-block running max/normaliser with rescaling is
+    the same softmax, only evaluated differently."""
+    q, k, v = small_case(Lq=37, Lk=70, D=8, seed=11)
+    ref = oracle.attention(q, k, v, 0.3, causal, window)
+    got = oracle.online_attention(q, k, v, 0.3, causal, window, block_n=block)
+    np.testing.assert_allclose(got[0], ref[0], atol=TIGHT, rtol=0)
+    np.testing.assert_allclose(got[1][np.isfinite(ref[1])], ref[1][np.isfinite(ref[1])], atol=TIGHT, rtol=0)
+    np.testing.assert_array_equal(np.isneginf(got[1]), np.isneginf(ref[1]))
+
+
+@pytest.mark.parametrize("causal,window", MASKS)
+@pytest.mark.parametrize("chunk", [1, 7, 32, 100])
+def test_p6_split_merge_equals_full(causal, window, chunk):
+    q, k, v = small_case(Lq=21, Lk=70, D=8, seed=12)
+    ref = oracle.attention(q, k, v, 0.3, causal, window)
+    got = oracle.split_merge_attention(q, k, v, 0.3, causal, window, chunk=chunk)
+    np.testing.assert_allclose(got[0], ref[0], atol=TIGHT, rtol=0)
+    fin = np.isfinite(ref[1])
+    np.testing.assert_allclose(got[1][fin], ref[1][fin], atol=TIGHT, rtol=0)
+
+
+# ---------------------------------------------------------------- P7
+
+def test_p7_key_shift_invariance():
+    """k_j + c for every j adds sc*q.c to every score of the row: out is
+    unchanged and lse shifts by sc*q.c."""
+    q, k, v = small_case(seed=13)
+    c = rnd((8,), 14)
+    sc = float(np.float32(0.3))
+    o1, l1 = oracle.attention(q, k, v, sc, True, 3)
+    o2, l2 = oracle.attention(q, k + c, v, sc, True, 3)
+    np.testing.assert_allclose(o2, o1, atol=1e-12, rtol=0)
+    shift = sc * np.einsum("bihd,d->bhi", q, c)
+    np.testing.assert_allclose(l2, l1 + shift, atol=1e-12, rtol=0)
+
+
+def test_p7_value_affine_and_constant():
+    q, k, v = small_case(seed=15)
+    o1, _ = oracle.attention(q, k, v, 0.3, False, -1)
+    o2, _ = oracle.attention(q, k, 2.5 * v - 1.25, 0.3, False, -1)
+    np.testing.assert_allclose(o2, 2.5 * o1 - 1.25, atol=1e-12, rtol=0)
+    const = np.broadcast_to(rnd((1, 1, 2, 8), 16), k.shape)
+    o3, _ = oracle.attention(q, k, const, 0.3, True, -1)
+    for h in range(4):
+        np.testing.assert_allclose(o3[:, :, h], np.broadcast_to(const[:, :1, h // 2], o3[:, :, h].shape), atol=1e-13)
+
+
+def test_p7_key_permutation_noncausal_and_zero_scale():
+    q, k, v = small_case(seed=17)
+    perm = np.random.default_rng(18).permutation(k.shape[1])
+    o1, l1 = oracle.attention(q, k, v, 0.3)
+    o2, l2 = oracle.attention(q, k[:, perm], v[:, perm], 0.3)
+    np.testing.assert_allclose(o2, o1, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(l2, l1, atol=1e-12, rtol=0)
+    o0, l0 = oracle.attention(q, k, v, 0.0)
+    for h in range(4):
+        np.testing.assert_allclose(o0[:, :, h], np.broadcast_to(v[:, :, h // 2].mean(1, keepdims=True), o0[:, :, h].shape), atol=1e-13)
+    np.testing.assert_allclose(l0, math.log(k.shape[1]), atol=1e-13)
+
+
+# ---------------------------------------------------------------- P8
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 2), (6, 1), (8, 8), (12, 2)])
+def test_p8_gqa_equals_mha_with_expanded_kv(Hq, Hkv):
+    """FA scenario 2, step 3: query heads of one group share one K/V head."""
+    q, k, v = small_case(Hq=Hq, Hkv=Hkv, seed=19)
+    o1, l1 = oracle.attention(q, k, v, 0.3, True, 5)
+    rep = Hq // Hkv
+    o2, l2 = oracle.attention(q, np.repeat(k, rep, axis=2), np.repeat(v, rep, axis=2), 0.3, True, 5)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+# ---------------------------------------------------------------- P9
+
+def test_p9_wide_window_is_plain_mask():
+    q, k, v = small_case(Lq=11, Lk=11, seed=20)
+    for causal in (True, False):
+        a = oracle.attention(q, k, v, 0.3, causal, -1)
+        b = oracle.attention(q, k, v, 0.3, causal, 10)
+        c = oracle.attention(q, k, v, 0.3, causal, 9)
+        np.testing.assert_array_equal(a[0], b[0])
+        assert not np.allclose(a[0], c[0])
+
+
+# ---------------------------------------------------------------- P10
+
+def _scatter_to_pool(K, V, ctx, bs, perm_seed, Hkv, D):
+    """Write contiguous per-sequence K/V into a permuted block pool."""
+    nblk = [-(-c // bs) for c in ctx]
+    nb = sum(nblk)
+    perm = np.random.default_rng(perm_seed).permutation(nb) if perm_seed is not None else np.arange(nb)
+    kc = np.full((nb, bs, Hkv, D), np.nan)
+    vc = np.full((nb, bs, Hkv, D), np.nan)
+    table = np.zeros((len(ctx), max(nblk)), dtype=np.int32)
+    o = 0
+    for s, c in enumerate(ctx):
+        for j in range(nblk[s]):
+            phys = perm[o + j]
+            table[s, j] = phys
+            n = min(bs, c - j * bs)
+            kc[phys, :n] = K[s][j * bs: j * bs + n]
+            vc[phys, :n] = V[s][j * bs: j * bs + n]
+        o += nblk[s]
+    return kc, vc, table
+
+
+def test_p10_paged_equals_dense_and_permutation_invariant():
+    """NEWS: the table changes where elements live, not which are attended."""
+    r = np.random.default_rng(21)
+    S, Hq, Hkv, D, bs = 5, 6, 2, 8, 4
+    ctx = [1, 4, 5, 13, 16]
+    K = [r.standard_normal((c, Hkv, D)) for c in ctx]
+    V = [r.standard_normal((c, Hkv, D)) for c in ctx]
+    q = r.standard_normal((S, Hq, D))
+    outs = []
+    for perm_seed in (None, 22, 23):
+        kc, vc, table = _scatter_to_pool(K, V, ctx, bs, perm_seed, Hkv, D)
+        o, l = oracle.decode_paged(q, kc, vc, table, np.array(ctx), bs, 0.35)
+        assert np.all(np.isfinite(o))  # NaN-filled unused slots are never read
+        outs.append((o, l))
+        for s in range(S):
+            ro, rl = oracle.attention(q[s][None, None], K[s][None], V[s][None], 0.35)
+            np.testing.assert_allclose(o[s], ro[0, 0], atol=TIGHT, rtol=0)
+            np.testing.assert_allclose(l[s], rl[0, :, 0], atol=TIGHT, rtol=0)
+    for o, l in outs[1:]:
+        np.testing.assert_array_equal(o, outs[0][0])
+        np.testing.assert_array_equal(l, outs[0][1])
+
+
+def test_p10_workload_generator_table_is_consistent():
+    cfg = CONFIGS["paged_decode"]
+    inp = paged_inputs(cfg)
+    ctx = inp.ctx_lens.numpy()
+    assert ctx.min() >= 512 and ctx.max() <= 4096
+    nblk = -(-ctx // 16)
+    assert inp.num_blocks == nblk.sum()
+    used = np.concatenate([inp.block_table[s, :nblk[s]].numpy() for s in range(cfg.num_seqs)])
+    assert np.array_equal(np.sort(used), np.arange(inp.num_blocks))  # a permutation of the pool
+
+
+# ---------------------------------------------------------------- P11
+
+def _torch_sdpa(q, k, v, sc, causal, window):
+    Lq, Lk = q.shape[1], k.shape[1]
+    Hq, Hkv = q.shape[2], k.shape[2]
+    qt = torch.from_numpy(np.ascontiguousarray(q.transpose(0, 2, 1, 3)))
+    kt = torch.from_numpy(np.ascontiguousarray(np.repeat(k, Hq // Hkv, 2).transpose(0, 2, 1, 3)))
+    vt = torch.from_numpy(np.ascontiguousarray(np.repeat(v, Hq // Hkv, 2).transpose(0, 2, 1, 3)))
+    i = torch.arange(Lq)[:, None] + (Lk - Lq)
+    j = torch.arange(Lk)[None, :]
+    m = torch.ones(Lq, Lk, dtype=torch.bool)
+    if causal:
+        m &= j <= i
+    if window >= 0:
+        m &= j >= i - window
+        if not causal:
+            m &= j <= i + window
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=m, scale=sc)
+    return o.numpy().transpose(0, 2, 1, 3)
+
+
+@pytest.mark.parametrize("name", ["tiny", "std512", "std512_causal", "vit"])
+def test_p11_library_sdpa_on_workloads(name):
+    """FA quick start / scenario 1: PyTorch's scaled_dot_product_attention is
+    the pages' own reference; here it runs on the CPU in float64."""
+    cfg = CONFIGS[name]
+    q, k, v = dense_inputs(cfg)
+    if name == "vit":  # a slice of the batch keeps the CPU suite short
+        q, k, v = q[:4], k[:4], v[:4]
+    q64, k64, v64 = (t.double().numpy() for t in (q, k, v))
+    sc = float(np.float32(cfg.scale))
+    out, _ = oracle.attention(q, k, v, cfg.scale, cfg.causal, cfg.window)
+    ref = _torch_sdpa(q64, k64, v64, sc, cfg.causal, cfg.window)
+    np.testing.assert_allclose(out, ref, atol=1e-12, rtol=0)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_p11_library_sdpa_random_shapes(seed):
+    r = np.random.default_rng(100 + seed)
+    Hkv = int(r.choice([1, 2]))
+    Hq = Hkv * int(r.choice([1, 3]))
+    Lq, Lk = int(r.integers(1, 40)), int(r.integers(1, 40))
+    causal = bool(r.integers(0, 2))
+    window = int(r.choice([-1, 0, 2, 7]))
+    if Lq > Lk and causal:
+        Lq = Lk  # torch returns NaN for rows with no visible key
+    if window >= 0 and not causal and Lq > Lk + window:
+        Lq = Lk
+    q, k, v = (t.double().numpy() for t in random_dense(2, Hq, Hkv, Lq, Lk, 16, "bf16", seed))
+    out, _ = oracle.attention(q, k, v, 0.25, causal, window)
+    ref = _torch_sdpa(q, k, v, 0.25, causal, window)
+    np.testing.assert_allclose(out, ref, atol=1e-12, rtol=0)
+
+
+# ---------------------------------------------------------------- sampled rows
+
+def test_rows_subset_matches_full():
+    q, k, v = small_case(Lq=30, Lk=30, seed=24)
+    full = oracle.attention(q, k, v, 0.3, True, 6)
+    rows = [0, 5, 17, 29]
+    part = oracle.attention(q, k, v, 0.3, True, 6, rows=rows)
+    np.testing.assert_array_equal(part[0], full[0][:, rows])
+    np.testing.assert_array_equal(part[1], full[1][:, :, rows])
