@@ -1,0 +1,144 @@
+/*
+ * attn.h - C ABI of the MI355X (gfx950) fused attention library (libattn.so).
+ *
+ * Two operations, both the scaled dot-product attention
+ *     out = softmax(Q K^T * scale) V
+ * of «Самовнимание, ядра CUDA и FlashAttention», section 1 (the Scores and
+ * Attention equations), evaluated the way its section 3 describes: Q, K and V
+ * are processed tile by tile on chip with an online softmax (running row
+ * maximum and row sum, partial outputs rescaled as the maximum grows), so the
+ * score matrix never reaches device memory; only the output and a small
+ * per-row statistic (the log-sum-exp) are written.
+ *
+ *   attn_fwd           - prefill/forward over dense [batch, seq, heads, dim]
+ *                        tensors, with the causal, sliding-window and MQA/GQA
+ *                        options of the flash-attn call on the «Flash
+ *                        Attention» page (quick start; scenario 2, steps 2-3).
+ *   attn_decode_paged  - one query token per sequence against a paged KV cache
+ *                        (fixed-size blocks plus a block table that maps each
+ *                        sequence's logical block to a physical block), as in
+ *                        the the-ai.news article, section «Внимание типа
+ *                        FlashAttention и постраничное внимание».
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    never allocates, frees or synchronises.  Calls enqueue work on `stream`
+ *    (a hipStream_t; NULL = the null stream) and return after the enqueue.
+ *  - Tensors are contiguous, row-major, last dimension innermost.  Element
+ *    type of q/k/v/out/caches is `dtype` (ATTN_F16 or ATTN_BF16); lse is fp32.
+ *  - Arguments are validated on the host before anything is launched.  On
+ *    failure the call returns a negative status, launches nothing and leaves
+ *    every output untouched.  No exception crosses this ABI.
+ *  - Supported: D in {64, 128}; Hq % Hkv == 0; block_size == 16 for decode;
+ *    tensor base pointers 16-byte aligned (lse 4-byte aligned).  The device
+ *    current on the calling thread must be a gfx950 GPU.
+ *  - Results: accumulation in fp32, probabilities rounded to `dtype` (round to
+ *    nearest even) before the P.V product, output rounded to `dtype` once.
+ *  - Calls are re-entrant; the library keeps no mutable state besides a
+ *    thread-safe per-device architecture check.
+ */
+#ifndef ATTN_MI355X_H
+#define ATTN_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { ATTN_F16 = 0, ATTN_BF16 = 1 } attn_dtype;
+
+enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = -1,        /* a required pointer is NULL                        */
+  ATTN_ERR_SHAPE = -2,       /* a size is negative/zero where it may not be, sizes
+                                are inconsistent (Hq % Hkv), a size product
+                                overflows, or scale is not finite                 */
+  ATTN_ERR_UNSUPPORTED = -3, /* D, dtype or block_size outside the supported set  */
+  ATTN_ERR_ALIGN = -4,       /* a tensor pointer is not suitably aligned          */
+  ATTN_ERR_WORKSPACE = -5,   /* decode workspace missing, misaligned or too small  */
+  ATTN_ERR_DEVICE = -6,      /* no current HIP device, or it is not gfx950         */
+  ATTN_ERR_HIP = -7          /* the HIP runtime reported an error at launch        */
+};
+
+/*
+ * attn_fwd - fused attention forward.
+ *
+ *   q    [B, Lq, Hq,  D]  dtype      k, v [B, Lk, Hkv, D]  dtype
+ *   out  [B, Lq, Hq,  D]  dtype      lse  [B, Hq, Lq] fp32, may be NULL
+ *
+ * out[b,i,h,:] = sum_j P[i,j] v[b,j,g,:] with g = h / (Hq/Hkv) (contiguous
+ * groups of query heads share a K/V head: MQA when Hkv = 1, GQA otherwise),
+ * P = row softmax of scale * q[b,i,h,:].k[b,j,g,:] over the keys j that row i
+ * may see:
+ *   - causal != 0: j <= i + (Lk - Lq)  (bottom-right alignment);
+ *   - window >= 0: j >= i + (Lk - Lq) - window, and, when not causal, also
+ *     j <= i + (Lk - Lq) + window (window_size = (window, window));
+ *   - window < 0: no sliding window.
+ * lse[b,h,i] = ln sum_j exp(scale * q.k_j) over the same keys.  A row that may
+ * see no key gets out = 0 and lse = -inf.  `scale` is used as given (the usual
+ * value is 1/sqrt(D)).
+ *
+ * B, Lq, Lk may be 0 (B = 0 or Lq = 0: nothing to do, returns ATTN_OK).  A
+ * pointer may be NULL only when its tensor is empty (q/out when B*Lq = 0,
+ * k/v when B*Lk = 0).
+ * Errors: ATTN_ERR_NULL (a non-empty q, k, v or out is NULL), ATTN_ERR_SHAPE,
+ * ATTN_ERR_UNSUPPORTED, ATTN_ERR_ALIGN, ATTN_ERR_DEVICE, ATTN_ERR_HIP.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+             int B, int Hq, int Hkv, int Lq, int Lk, int D,
+             float scale, int causal, int window, int dtype, void* stream);
+
+/*
+ * attn_decode_paged - one new query token per sequence against its paged
+ * KV cache.
+ *
+ *   q, out       [num_seqs, Hq, D]                       dtype
+ *   k_cache,
+ *   v_cache      [num_blocks, block_size, Hkv, D]         dtype
+ *   block_table  [num_seqs, max_blocks_per_seq]           int32
+ *   ctx_lens     [num_seqs]                               int32
+ *   lse          [num_seqs, Hq]  fp32, may be NULL
+ *   workspace    >= attn_decode_paged_workspace_size(...) bytes, 16-byte aligned
+ *
+ * Sequence s attends the positions p in [0, ctx_lens[s]) of its own cache;
+ * position p lives in physical block block_table[s, p / block_size] at slot
+ * p % block_size.  The result equals attn_fwd on the gathered contiguous K/V
+ * with Lq = 1 (paging moves elements, it does not change which are attended).
+ *
+ * block_table and ctx_lens live in device memory, so their contents are caller
+ * preconditions that the host cannot check without a synchronisation:
+ * 0 <= ctx_lens[s] <= max_blocks_per_seq * block_size and every entry used by a
+ * sequence in [0, num_blocks).  Violations never make the kernels read outside
+ * the given buffers (lengths and block ids are clamped) but give unspecified
+ * values.  A sequence with ctx_len = 0 gets out = 0 and lse = -inf.
+ * The workspace holds per-chunk partial results between the two kernels of
+ * one call; calls that share a workspace must be ordered on one stream.
+ * num_seqs = 0 is a no-op (pointers may then be NULL).
+ * Errors: ATTN_ERR_NULL, ATTN_ERR_SHAPE, ATTN_ERR_UNSUPPORTED, ATTN_ERR_ALIGN,
+ * ATTN_ERR_WORKSPACE, ATTN_ERR_DEVICE, ATTN_ERR_HIP.
+ */
+int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_table, const int32_t* ctx_lens, int block_size,
+                      void* out, float* lse,
+                      int num_seqs, int Hq, int Hkv, int D, int max_blocks_per_seq, int num_blocks,
+                      float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of workspace attn_decode_paged needs for these sizes (a pure host
+ * function; no device is touched).  Returns 0 when nothing needs a workspace
+ * (num_seqs = 0) or when the arguments are invalid.
+ */
+size_t attn_decode_paged_workspace_size(int num_seqs, int Hq, int D, int max_blocks_per_seq,
+                                        int block_size);
+
+/* A static, human-readable description of a status code (never NULL). */
+const char* attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_MI355X_H */

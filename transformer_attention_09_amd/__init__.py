@@ -1,0 +1,205 @@
+"""Fused attention for AMD Instinct MI355X (gfx950): Python binding of libattn.so.
+
+Every step of the computation runs in the HIP kernels of libattn.so; this
+module only marshals torch tensors (device memory and the current stream) into
+the C ABI declared in include/attn.h, with the same entry-point names:
+
+    attn_fwd(q, k, v, ...)                  q [B,Lq,Hq,D], k/v [B,Lk,Hkv,D]
+    attn_decode_paged(q, k_cache, ...)      q [S,Hq,D], caches [N,16,Hkv,D]
+    attn_decode_paged_workspace_size(...)
+    attn_status_string(status)
+
+There is no fallback: if the library is missing or the device is not a
+gfx950 GPU the calls raise.  Build the library with
+``python -m transformer_attention_09_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+from typing import Optional
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+
+ATTN_F16, ATTN_BF16 = 0, 1
+STATUS = {
+    0: "ATTN_OK",
+    -1: "ATTN_ERR_NULL",
+    -2: "ATTN_ERR_SHAPE",
+    -3: "ATTN_ERR_UNSUPPORTED",
+    -4: "ATTN_ERR_ALIGN",
+    -5: "ATTN_ERR_WORKSPACE",
+    -6: "ATTN_ERR_DEVICE",
+    -7: "ATTN_ERR_HIP",
+}
+EXPORTED = ("attn_fwd", "attn_decode_paged", "attn_decode_paged_workspace_size", "attn_status_string")
+
+_lib = None
+_lock = threading.Lock()
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({_status_text(status)})")
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libattn.so once; raise if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    f"{LIB_PATH} is missing: build it with `python -m transformer_attention_09_amd.build`")
+            lib = ctypes.CDLL(LIB_PATH)
+            vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+            lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32, i32, vp]
+            lib.attn_fwd.restype = i32
+            lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
+                                              f32, i32, vp, sz, vp]
+            lib.attn_decode_paged.restype = i32
+            lib.attn_decode_paged_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+            lib.attn_decode_paged_workspace_size.restype = sz
+            lib.attn_status_string.argtypes = [i32]
+            lib.attn_status_string.restype = ctypes.c_char_p
+            _lib = lib
+    return _lib
+
+
+def _status_text(status: int) -> str:
+    try:
+        return load_library().attn_status_string(status).decode()
+    except Exception:  # noqa: BLE001 - message only
+        return "?"
+
+
+def attn_status_string(status: int) -> str:
+    return load_library().attn_status_string(int(status)).decode()
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.float16:
+        return ATTN_F16
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; expected float16 or bfloat16")
+
+
+def _stream_handle(stream) -> Optional[int]:
+    import torch
+
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream if hasattr(s, "cuda_stream") else int(s)
+
+
+def _require_cuda(name, t):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def attn_fwd(q, k, v, out=None, lse=None, scale: Optional[float] = None, causal: bool = False,
+             window: int = -1, stream=None, return_lse: bool = True):
+    """Fused attention forward; returns (out, lse) (lse None if not requested).
+
+    q [B,Lq,Hq,D], k/v [B,Lk,Hkv,D]; scale defaults to 1/sqrt(D); window < 0
+    disables the sliding window; causal masking is aligned bottom-right.
+    """
+    import torch
+
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _require_cuda(n, t)
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
+        raise ValueError("expected q [B,Lq,Hq,D] and k, v [B,Lk,Hkv,D] of equal shape")
+    B, Lq, Hq, D = q.shape
+    Bk, Lk, Hkv, Dk = k.shape
+    if Bk != B or Dk != D or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v disagree in batch, head dim or dtype")
+    if out is None:
+        out = torch.empty_like(q)
+    _require_cuda("out", out)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _require_cuda("lse", lse)
+        if lse.shape != (B, Hq, Lq) or lse.dtype != torch.float32:
+            raise ValueError("lse must be float32 [B,Hq,Lq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    st = load_library().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                 lse.data_ptr() if lse is not None else None,
+                                 B, Hq, Hkv, Lq, Lk, D, float(scale), int(bool(causal)), int(window),
+                                 _dtype_code(q), _stream_handle(stream))
+    if st != 0:
+        raise AttnError(st, "attn_fwd")
+    return out, lse
+
+
+def attn_decode_paged_workspace_size(num_seqs: int, Hq: int, D: int, max_blocks_per_seq: int,
+                                     block_size: int = 16) -> int:
+    return int(load_library().attn_decode_paged_workspace_size(num_seqs, Hq, D, max_blocks_per_seq, block_size))
+
+
+def attn_decode_paged(q, k_cache, v_cache, block_table, ctx_lens, out=None, lse=None,
+                      scale: Optional[float] = None, workspace=None, stream=None,
+                      return_lse: bool = True, check_table: bool = False):
+    """Paged-KV decode; returns (out, lse).
+
+    q [S,Hq,D]; k_cache/v_cache [num_blocks, block_size, Hkv, D]; block_table
+    int32 [S, max_blocks_per_seq]; ctx_lens int32 [S].  check_table=True
+    copies the table and lengths to the host and validates them first (it
+    synchronises; meant for tests).
+    """
+    import torch
+
+    for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("block_table", block_table),
+                 ("ctx_lens", ctx_lens)):
+        _require_cuda(n, t)
+    if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("expected q [S,Hq,D] and caches [N,block_size,Hkv,D] of equal shape")
+    S, Hq, D = q.shape
+    num_blocks, bs, Hkv, Dk = k_cache.shape
+    if Dk != D or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("q and caches disagree in head dim or dtype")
+    if block_table.dtype != torch.int32 or ctx_lens.dtype != torch.int32:
+        raise ValueError("block_table and ctx_lens must be int32")
+    if block_table.dim() != 2 or block_table.shape[0] != S or ctx_lens.shape != (S,):
+        raise ValueError("block_table must be [S, max_blocks_per_seq] and ctx_lens [S]")
+    mbps = block_table.shape[1]
+    if check_table:
+        ctx = ctx_lens.cpu()
+        tab = block_table.cpu()
+        if ctx.numel() and (int(ctx.min()) < 0 or int(ctx.max()) > mbps * bs):
+            raise ValueError("ctx_lens outside [0, max_blocks_per_seq * block_size]")
+        for s in range(S):
+            n = -(-int(ctx[s]) // bs)
+            if n and (int(tab[s, :n].min()) < 0 or int(tab[s, :n].max()) >= num_blocks):
+                raise ValueError(f"block_table row {s} points outside the pool")
+    if out is None:
+        out = torch.empty_like(q)
+    _require_cuda("out", out)
+    if lse is None and return_lse:
+        lse = torch.empty((S, Hq), dtype=torch.float32, device=q.device)
+    need = attn_decode_paged_workspace_size(S, Hq, D, mbps, bs) if S else 0
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    st = load_library().attn_decode_paged(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                          block_table.data_ptr(), ctx_lens.data_ptr(), bs,
+                                          out.data_ptr(), lse.data_ptr() if lse is not None else None,
+                                          S, Hq, Hkv, D, mbps, num_blocks, float(scale), _dtype_code(q),
+                                          ws_ptr, ws_bytes, _stream_handle(stream))
+    if st != 0:
+        raise AttnError(st, "attn_decode_paged")
+    return out, lse

@@ -1,0 +1,83 @@
+// Shared device helpers for the gfx950 attention kernels.
+//
+// MFMA lane layouts used throughout (CDNA4, wave64; verified on the device):
+//  v_mfma_f32_32x32x16_{bf16,f16}: lane l holds A[l%32][8*(l/32)+e] and
+//    B[8*(l/32)+e][l%32] (e = 0..7); accumulator register r of lane l is
+//    C[8*(r/4) + 4*(l/32) + r%4][l%32].
+//  v_mfma_f32_16x16x32_{bf16,f16}: lane l holds A[l%16][8*(l/16)+e] and
+//    B[8*(l/16)+e][l%16]; register r of lane l is C[4*(l/16) + r][l%16].
+//  ds_read_b64_tr_b16: inside each group of 16 lanes, lane i receives
+//    element i%4 of the 8-byte chunk addressed by group lane 4*e + i/4, for
+//    e = 0..3.  Pointing group lane j at row (r0 + j/4), columns
+//    (c0 + 4*(j%4) .. +3) of a row-major 16-bit matrix hands lane i the
+//    column c0 + i of rows r0..r0+3: a transposed fetch of a 4 x 16 block.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+// Element-type traits: storage is 16 bits; arithmetic is fp32 with MFMA.
+struct BF16 {
+  typedef __bf16 elem;
+  typedef bf16x8 vec8;
+  typedef bf16x4 vec4;
+  static __device__ __forceinline__ f32x16 mfma32(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma16(vec8 a, vec8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ vec4 read_tr(const void* lds) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(vec4, lds));
+  }
+  static __device__ __forceinline__ elem cvt(float x) { return (elem)x; }  // RNE
+  static __device__ __forceinline__ float to_f32(elem x) { return (float)x; }
+};
+
+struct F16 {
+  typedef _Float16 elem;
+  typedef f16x8 vec8;
+  typedef f16x4 vec4;
+  static __device__ __forceinline__ f32x16 mfma32(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma16(vec8 a, vec8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ vec4 read_tr(const void* lds) {
+    typedef __fp16 h4 __attribute__((ext_vector_type(4)));
+    return __builtin_bit_cast(vec4, __builtin_amdgcn_ds_read_tr16_b64_v4f16(LDS_PTR(h4, lds)));
+  }
+  static __device__ __forceinline__ elem cvt(float x) { return (elem)x; }  // RNE
+  static __device__ __forceinline__ float to_f32(elem x) { return (float)x; }
+};
+
+template <typename V4, typename V8>
+__device__ __forceinline__ V8 cat4(V4 lo, V4 hi) {
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ float wave_xor_max(float x, int mask) {
+  return fmaxf(x, __shfl_xor(x, mask, 64));
+}
+__device__ __forceinline__ float wave_xor_sum(float x, int mask) {
+  return x + __shfl_xor(x, mask, 64);
+}
+
+constexpr float kLn2 = 0.69314718055994530942f;
+
+}  // namespace attn

@@ -1,0 +1,293 @@
+// Fused attention forward for gfx950 (CDNA4): softmax(Q K^T * scale) V.
+//
+// The method is the tiled, fused evaluation of «Самовнимание, ядра CUDA и
+// FlashAttention», section 3: Q, K and V are cut into blocks that live on
+// chip, each K/V block updates a running row maximum and row sum (the online
+// softmax) and rescales the partial output, and only the final output plus
+// the per-row log-sum-exp ("small normalisation statistics") go back to
+// device memory.  The the-ai.news article (section «Внимание типа
+// FlashAttention и постраничное внимание») states the same per-block loop:
+// partial scores, updated softmax statistics, output accumulated on chip.
+// The pages' kernels (64x64 tiles, a K-loop matmul on tensor cores, «Как
+// ускорить нейросети…», section on kernel internals) are prior art for other
+// hardware; this kernel is laid out for CDNA4 as follows.
+//
+// Work decomposition
+//   One work-group = 4 waves = 128 query rows of one (batch, query head); each
+//   wave owns 32 rows.  K/V tiles of 64 keys are staged through LDS (double
+//   buffered; global loads for tile t+1 are in flight while tile t computes)
+//   and shared by the 4 waves.  Causal and sliding-window masks are applied
+//   as a key-tile range [t_lo, t_hi) per work-group, so fully masked tiles are
+//   never loaded; a wave skips tiles that its own rows cannot see, and only
+//   tiles that straddle a mask edge (or the end of the keys) pay for an
+//   element-wise mask.  Causal work-groups are issued heaviest first.
+//
+// Per 64-key tile and wave (all MFMA 32x32x16, fp32 accumulate):
+//   S^T = K Q^T  : A = K rows from LDS, B = the wave's Q rows (registers).
+//                  The transposed product puts one query per lane column, so
+//                  a row's maximum and sum need one cross-lane step (lane ^ 32).
+//   online softmax in base 2: x = s * scale * log2(e), p = 2^(x - m).
+//   O^T += V^T P^T: A = V^T fetched from the natural [key][d] LDS tile with
+//                  the LDS transpose read, B = P straight from the S^T
+//                  accumulators (rounded to the input type), no shuffles.
+//
+// LDS: 2 stages x (K tile + V tile) x 64 x D x 2 B = 64 KiB at D = 128, so two
+// work-groups fit in the 160 KiB of a CU.  16-byte chunks of each row are
+// XOR-swizzled by row so the MFMA operand reads hit distinct banks.
+#include "common.h"
+#include "internal.h"
+
+namespace attn {
+
+template <int D>
+struct FwdCfg {
+  static constexpr int BM = kPrefillBlockM;  // query rows per work-group
+  static constexpr int BN = 64;              // keys per tile
+  static constexpr int NT = 256;             // threads (4 waves)
+  static constexpr int CPR = D / 8;          // 16-byte chunks per K/V row
+  static constexpr int RPP = NT / CPR;       // rows per staging pass
+  static constexpr int KPT = BN / RPP;       // staging passes per tile
+  static constexpr int KSTEPS = D / 16;      // k-steps of S^T = K Q^T
+  static constexpr int DB = D / 32;          // 32-row blocks of O^T
+  static constexpr int TILE = BN * D;        // elements per K or V tile
+};
+
+// Swizzle of the 16-byte chunk index inside a K row.  K operand reads take
+// one chunk from 32 consecutive rows; any 16 consecutive rows map to distinct
+// chunks (and any 8 to distinct chunks mod 8).
+template <int D>
+__device__ __forceinline__ int k_swz(int r) {
+  if constexpr (D == 128) return r & 15;
+  else return (r ^ (r >> 3)) & 7;
+}
+// Swizzle inside a V row.  A transposed read of a 16-lane group touches 4
+// consecutive rows (r % 4 = 0..3) x 2 adjacent chunks; two groups of a half
+// wave touch 4 adjacent chunks.  For D = 128 the offsets {0, 6, 10, 12} keep
+// both the 8 and the 16 touched chunks of a row quad on distinct banks.
+template <int D>
+__device__ __forceinline__ int v_swz(int r) {
+  if constexpr (D == 128) return ((r & 1) * 6) ^ (((r >> 1) & 1) * 10);
+  else return (r & 3) << 1;
+}
+
+template <typename TT, int D>
+__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
+  using C = FwdCfg<D>;
+  using E = typename TT::elem;
+  using V8 = typename TT::vec8;
+  using V4 = typename TT::vec4;
+  __shared__ __attribute__((aligned(16))) E smem[2 * 2 * C::TILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int hh = lane >> 5, l32 = lane & 31;
+
+  // ---- which (q-block, head, batch)
+  const int per_qb = a.Hq * a.B;
+  const int qb_rank = blockIdx.x / per_qb;
+  const int rem = blockIdx.x - qb_rank * per_qb;
+  const int hq = rem % a.Hq, b = rem / a.Hq;
+  const int qb = a.causal ? (a.n_qblocks - 1 - qb_rank) : qb_rank;
+  const int g = hq / a.group;
+  const int q0 = qb * C::BM;
+  const int off = a.Lk - a.Lq;  // bottom-right alignment of the causal diagonal
+  const int W = a.window;
+
+  // ---- key-tile range of the whole work-group
+  const int row_hi = min(q0 + C::BM, a.Lq) - 1;
+  int j_lo = 0, j_hi = a.Lk - 1;
+  if (a.causal) j_hi = min(j_hi, row_hi + off);
+  if (W >= 0) {
+    j_lo = max(j_lo, q0 + off - W);
+    if (!a.causal) j_hi = min(j_hi, row_hi + off + W);
+  }
+  const int t_lo = j_lo / C::BN;
+  const int t_hi = (j_hi >= j_lo) ? j_hi / C::BN + 1 : t_lo;
+
+  // ---- this lane's query row and its Q operand (B of S^T = K Q^T)
+  const int qi = q0 + wave * 32 + l32;
+  const E* qbase = (const E*)a.q;
+  V8 qf[C::KSTEPS];
+  {
+    const E* qrow = qbase + ((size_t)((size_t)b * a.Lq + qi) * a.Hq + hq) * D;
+#pragma unroll
+    for (int s = 0; s < C::KSTEPS; ++s) {
+      if (qi < a.Lq) qf[s] = *(const V8*)(qrow + 16 * s + 8 * hh);
+      else qf[s] = V8{};
+    }
+  }
+  const int wr_lo = q0 + wave * 32;
+  const int wr_hi = min(wr_lo + 31, a.Lq - 1);
+  const bool wave_live = wr_lo < a.Lq;
+
+  // ---- staging: thread -> (chunk sc, rows sr + i * RPP)
+  const int sc = tid % C::CPR, sr = tid / C::CPR;
+  const size_t kv_rs = (size_t)a.Hkv * D;  // elements between consecutive keys
+  const E* kb = (const E*)a.k + ((size_t)b * a.Lk * a.Hkv + g) * D;
+  const E* vb = (const E*)a.v + ((size_t)b * a.Lk * a.Hkv + g) * D;
+  uint4 kreg[C::KPT], vreg[C::KPT];
+  auto gload = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < C::KPT; ++i) {
+      const int j = t * C::BN + sr + i * C::RPP;
+      if (j < a.Lk) {
+        kreg[i] = *(const uint4*)(kb + j * kv_rs + sc * 8);
+        vreg[i] = *(const uint4*)(vb + j * kv_rs + sc * 8);
+      } else {
+        kreg[i] = make_uint4(0, 0, 0, 0);
+        vreg[i] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto sstore = [&](int stage) {
+    E* ks = smem + stage * 2 * C::TILE;
+    E* vs = ks + C::TILE;
+#pragma unroll
+    for (int i = 0; i < C::KPT; ++i) {
+      const int r = sr + i * C::RPP;
+      *(uint4*)(ks + r * D + ((sc ^ k_swz<D>(r)) << 3)) = kreg[i];
+      *(uint4*)(vs + r * D + ((sc ^ v_swz<D>(r)) << 3)) = vreg[i];
+    }
+  };
+
+  f32x16 oacc[C::DB];
+#pragma unroll
+  for (int d = 0; d < C::DB; ++d) oacc[d] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float sl2 = a.scale_log2;
+
+  if (t_lo < t_hi) {
+    gload(t_lo);
+    sstore(0);
+  }
+  __syncthreads();
+
+  for (int t = t_lo; t < t_hi; ++t) {
+    const int stage = (t - t_lo) & 1;
+    if (t + 1 < t_hi) gload(t + 1);
+    const int jt = t * C::BN;
+
+    // Can any row of this wave see a key of the tile?  Does every row see all?
+    bool any = wave_live;
+    if (a.causal && jt > wr_hi + off) any = false;
+    if (W >= 0 && jt + C::BN - 1 < wr_lo + off - W) any = false;
+    if (W >= 0 && !a.causal && jt > wr_hi + off + W) any = false;
+    const bool full = (jt + C::BN <= a.Lk) && (!a.causal || jt + C::BN - 1 <= wr_lo + off) &&
+                      (W < 0 || jt >= wr_hi + off - W) &&
+                      (W < 0 || a.causal || jt + C::BN - 1 <= wr_lo + off + W);
+
+    if (any) {
+      const E* ks = smem + stage * 2 * C::TILE;
+      const E* vs = ks + C::TILE;
+
+      // S^T = K Q^T for the tile's two 32-key halves.
+      f32x16 sacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int s = 0; s < C::KSTEPS; ++s) {
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+          const int r = kh * 32 + l32;
+          const V8 kf = *(const V8*)(ks + r * D + (((2 * s + hh) ^ k_swz<D>(r)) << 3));
+          sacc[kh] = TT::mfma32(kf, qf[s], sacc[kh]);
+        }
+      }
+
+      // Scale to base 2, mask, running maximum (lane and lane^32 share a row).
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = sacc[kh][r] * sl2;
+          if (!full) {
+            const int j = jt + kh * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+            const int dj = j - (qi + off);
+            bool ok = j < a.Lk;
+            if (a.causal) ok = ok && dj <= 0;
+            if (W >= 0) ok = ok && dj >= -W && (a.causal || dj <= W);
+            x = ok ? x : -INFINITY;
+          }
+          sacc[kh][r] = x;
+          mx = fmaxf(mx, x);
+        }
+      }
+      mx = wave_xor_max(mx, 32);
+      const float m_new = fmaxf(m_run, mx);
+      const float base = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - base);
+
+      // P = 2^(x - m), row sums, and P as the B operand of O^T += V^T P^T.
+      V8 pf[4];
+      float rs = 0.f;
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(sacc[kh][r] - base);
+          rs += p;
+          pf[2 * kh + (r >> 3)][r & 7] = TT::cvt(p);
+        }
+      }
+      l_run = l_run * alpha + rs;
+      m_run = m_new;
+#pragma unroll
+      for (int d = 0; d < C::DB; ++d) oacc[d] *= alpha;
+
+      // O^T += V^T P^T, 16 keys per MFMA k-step.  Key order inside a step is
+      // the one the S^T accumulator hands out: operand index 8*hh + e is key
+      // 16*s + 8*(e/4) + 4*hh + e%4.  The two transposed reads fetch exactly
+      // those V rows for column d = 32*db + 16*(group&1) + (lane&15).
+      const int j16 = lane & 15, grp = lane >> 4;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int r0 = 16 * s + 4 * hh + (j16 >> 2);
+        const int r1 = r0 + 8;
+#pragma unroll
+        for (int d = 0; d < C::DB; ++d) {
+          const int col = 32 * d + 16 * (grp & 1) + 4 * (j16 & 3);
+          const int ch = col >> 3, hf = (col >> 2) & 1;
+          const E* p0 = vs + r0 * D + (((ch ^ v_swz<D>(r0)) << 3) + 4 * hf);
+          const E* p1 = vs + r1 * D + (((ch ^ v_swz<D>(r1)) << 3) + 4 * hf);
+          const V8 vf = cat4<V4, V8>(TT::read_tr(p0), TT::read_tr(p1));
+          oacc[d] = TT::mfma32(vf, pf[s], oacc[d]);
+        }
+      }
+    }
+
+    if (t + 1 < t_hi) sstore(stage ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: normalise, store O in the input type, and the log-sum-exp
+  const float lt = wave_xor_sum(l_run, 32);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if (qi < a.Lq) {
+    E* orow = (E*)a.o + ((size_t)((size_t)b * a.Lq + qi) * a.Hq + hq) * D;
+#pragma unroll
+    for (int d = 0; d < C::DB; ++d) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        typename TT::vec4 ov;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ov[e] = TT::cvt(oacc[d][4 * q4 + e] * inv);
+        *(typename TT::vec4*)(orow + 32 * d + 8 * q4 + 4 * hh) = ov;
+      }
+    }
+    if (a.lse != nullptr && hh == 0)
+      a.lse[((size_t)b * a.Hq + hq) * a.Lq + qi] = lt > 0.f ? (m_run + log2f(lt)) * kLn2 : -INFINITY;
+  }
+}
+
+template <typename TT, int D>
+static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
+  const long long blocks = (long long)a.n_qblocks * a.Hq * a.B;
+  hipLaunchKernelGGL((fwd_kernel<TT, D>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd(const FwdArgs& a, int D, int dtype, hipStream_t stream) {
+  if (dtype == 1) return D == 128 ? launch_fwd_t<BF16, 128>(a, stream) : launch_fwd_t<BF16, 64>(a, stream);
+  return D == 128 ? launch_fwd_t<F16, 128>(a, stream) : launch_fwd_t<F16, 64>(a, stream);
+}
+
+}  // namespace attn
