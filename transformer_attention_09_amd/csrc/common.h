@@ -63,6 +63,17 @@ struct F16 {
   static __device__ __forceinline__ float to_f32(elem x) { return (float)x; }
 };
 
+// Raw buffer access: a 128-bit resource (base, byte range) lets a load outside
+// [0, bytes) return zeros without a branch.  The third word is the gfx9-family
+// default (raw, untyped, 32-bit data).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
 template <typename V4, typename V8>
 __device__ __forceinline__ V8 cat4(V4 lo, V4 hi) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -71,11 +82,26 @@ __device__ __forceinline__ V8 cat4(V4 lo, V4 hi) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-__device__ __forceinline__ float wave_xor_max(float x, int mask) {
-  return fmaxf(x, __shfl_xor(x, mask, 64));
+// Reductions across lane l and lane l^32 (or l^16).  v_permlane32_swap trades
+// the two 32-lane halves between its operands (v_permlane16_swap trades the
+// odd and even 16-lane rows); with both operands = x, one result holds x[l]
+// and the other x[l^32] (x[l^16]) in every lane, so their max/sum is the
+// pairwise reduction, in one VALU op and without the LDS crossbar.
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ float wave_xor_sum(float x, int mask) {
-  return x + __shfl_xor(x, mask, 64);
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 constexpr float kLn2 = 0.69314718055994530942f;

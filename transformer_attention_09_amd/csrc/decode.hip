@@ -140,8 +140,8 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecArgs a) {
       mx = fmaxf(mx, x);
     }
   }
-  mx = wave_xor_max(mx, 16);
-  mx = wave_xor_max(mx, 32);
+  mx = max_xor16(mx);
+  mx = max_xor32(mx);
   const float base = (mx == -INFINITY) ? 0.f : mx;
 
   // P (B operand of O^T = V^T P^T): k index 8*g4 + e is
@@ -157,8 +157,8 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecArgs a) {
       pf[i >> 1][4 * (i & 1) + r] = TT::cvt(p);
     }
   }
-  lsum = wave_xor_sum(lsum, 16);
-  lsum = wave_xor_sum(lsum, 32);
+  lsum = sum_xor16(lsum);
+  lsum = sum_xor32(lsum);
 
   // Stage this wave's V blocks in LDS ([block][slot][d], chunk-swizzled);
   // slots past the context are written as zeros.

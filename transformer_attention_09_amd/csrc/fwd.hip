@@ -57,17 +57,38 @@ struct FwdCfg {
 // chunks (and any 8 to distinct chunks mod 8).
 template <int D>
 __device__ __forceinline__ int k_swz(int r) {
+  // Depends on r % 32 only, so the two 32-row halves of a tile share offsets.
   if constexpr (D == 128) return r & 15;
-  else return (r ^ (r >> 3)) & 7;
+  else return (r ^ ((r >> 3) & 3)) & 7;
 }
 // Swizzle inside a V row.  A transposed read of a 16-lane group touches 4
 // consecutive rows (r % 4 = 0..3) x 2 adjacent chunks; two groups of a half
 // wave touch 4 adjacent chunks.  For D = 128 the offsets {0, 6, 10, 12} keep
 // both the 8 and the 16 touched chunks of a row quad on distinct banks.
+// Depends on r % 4 only.
 template <int D>
 __device__ __forceinline__ int v_swz(int r) {
   if constexpr (D == 128) return ((r & 1) * 6) ^ (((r >> 1) & 1) * 10);
   else return (r & 3) << 1;
+}
+
+// The running maximum used as the exponent base is only moved when a row's
+// new maximum exceeds it by more than this (base-2 units): probabilities then
+// stay below 2^8, exact enough in fp32 and in the 16-bit P operand, and the
+// rescale of the output accumulator is skipped on almost every tile.
+constexpr float kRescaleThreshold = 8.0f;
+
+template <typename TT>
+__device__ __forceinline__ uint32_t pack2(float a, float b);
+template <>
+__device__ __forceinline__ uint32_t pack2<BF16>(float a, float b) {
+  typedef __bf16 v2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, (v2){(__bf16)a, (__bf16)b});
+}
+template <>
+__device__ __forceinline__ uint32_t pack2<F16>(float a, float b) {
+  typedef _Float16 v2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, (v2){(_Float16)a, (_Float16)b});
 }
 
 template <typename TT, int D>
@@ -81,6 +102,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, l32 = lane & 31;
+  const int j16 = lane & 15, grp = lane >> 4;
 
   // ---- which (q-block, head, batch)
   const int per_qb = a.Hq * a.B;
@@ -104,39 +126,75 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   const int t_lo = j_lo / C::BN;
   const int t_hi = (j_hi >= j_lo) ? j_hi / C::BN + 1 : t_lo;
 
-  // ---- this lane's query row and its Q operand (B of S^T = K Q^T)
+  // ---- this lane's query row and its Q operand (B of S^T = K Q^T).
+  // The kernel keeps the base-2 scale positive: a negative scale is moved
+  // into Q (an exact sign flip) and a zero scale zeroes Q.
   const int qi = q0 + wave * 32 + l32;
-  const E* qbase = (const E*)a.q;
+  float sl2 = a.scale_log2;
+  uint32_t qsign = 0u, qkeep = 0xffffffffu;
+  if (sl2 < 0.f) { qsign = 0x80008000u; sl2 = -sl2; }
+  if (sl2 == 0.f) { qkeep = 0u; sl2 = 1.f; }
   V8 qf[C::KSTEPS];
   {
-    const E* qrow = qbase + ((size_t)((size_t)b * a.Lq + qi) * a.Hq + hq) * D;
+    // Rows q0.. of this head: row i at (i - q0) * Hq * D elements; rows past
+    // Lq read as zeros through the resource range.
+    const E* qbase = (const E*)a.q + ((size_t)((size_t)b * a.Lq + q0) * a.Hq + hq) * D;
+    const rsrc_t qr = make_rsrc(qbase, (uint32_t)(((size_t)(a.Lq - q0 - 1) * a.Hq + 1) * D * sizeof(E)));
+    const uint32_t qo = (uint32_t)(((size_t)(wave * 32 + l32) * a.Hq * D + 8 * hh) * sizeof(E));
 #pragma unroll
     for (int s = 0; s < C::KSTEPS; ++s) {
-      if (qi < a.Lq) qf[s] = *(const V8*)(qrow + 16 * s + 8 * hh);
-      else qf[s] = V8{};
+      uint4 w = buf_load16(qr, qo + 32 * s);
+      w.x = (w.x ^ qsign) & qkeep; w.y = (w.y ^ qsign) & qkeep;
+      w.z = (w.z ^ qsign) & qkeep; w.w = (w.w ^ qsign) & qkeep;
+      qf[s] = __builtin_bit_cast(V8, w);
     }
+  }
+  // Keys this row may see: [jlo_row, jhi_row] (empty when jhi_row < jlo_row).
+  int jlo_row = 0, jhi_row = a.Lk - 1;
+  if (a.causal) jhi_row = min(jhi_row, qi + off);
+  if (W >= 0) {
+    jlo_row = max(jlo_row, qi + off - W);
+    if (!a.causal) jhi_row = min(jhi_row, qi + off + W);
   }
   const int wr_lo = q0 + wave * 32;
   const int wr_hi = min(wr_lo + 31, a.Lq - 1);
   const bool wave_live = wr_lo < a.Lq;
+
+  // ---- per-lane LDS element offsets inside a stage (hoisted out of the loop)
+  int koff[C::KSTEPS];  // K operand of k-step s, first 32-key half (+32*D for the second)
+#pragma unroll
+  for (int s = 0; s < C::KSTEPS; ++s) koff[s] = l32 * D + (((2 * s + hh) ^ k_swz<D>(l32)) << 3);
+  int voff[C::DB];      // V transposed read for d-block d, rows 4*hh + j16/4 (+16*s, +8)
+  {
+    const int r = 4 * hh + (j16 >> 2);
+#pragma unroll
+    for (int d = 0; d < C::DB; ++d) {
+      const int col = 32 * d + 16 * (grp & 1) + 4 * (j16 & 3);
+      voff[d] = C::TILE + r * D + ((((col >> 3) ^ v_swz<D>(r)) << 3) + 4 * ((col >> 2) & 1));
+    }
+  }
 
   // ---- staging: thread -> (chunk sc, rows sr + i * RPP)
   const int sc = tid % C::CPR, sr = tid / C::CPR;
   const size_t kv_rs = (size_t)a.Hkv * D;  // elements between consecutive keys
   const E* kb = (const E*)a.k + ((size_t)b * a.Lk * a.Hkv + g) * D;
   const E* vb = (const E*)a.v + ((size_t)b * a.Lk * a.Hkv + g) * D;
+  // Byte offset of this thread's chunk inside a tile (rows sr + i*RPP).
+  const uint32_t so = (uint32_t)(((size_t)sr * kv_rs + sc * 8) * sizeof(E));
+  const uint32_t so_step = (uint32_t)((size_t)C::RPP * kv_rs * sizeof(E));
   uint4 kreg[C::KPT], vreg[C::KPT];
   auto gload = [&](int t) {
+    // Resources start at the tile's first key and end after key Lk-1, so
+    // rows past the end of the keys load as zeros.
+    const size_t jt = (size_t)t * C::BN;
+    const size_t bytes = (((size_t)(a.Lk - jt) - 1) * kv_rs + D) * sizeof(E);
+    const uint32_t nb = bytes > 0x7fffffffu ? 0x7fffffffu : (uint32_t)bytes;
+    const rsrc_t kr = make_rsrc(kb + jt * kv_rs, nb);
+    const rsrc_t vr = make_rsrc(vb + jt * kv_rs, nb);
 #pragma unroll
     for (int i = 0; i < C::KPT; ++i) {
-      const int j = t * C::BN + sr + i * C::RPP;
-      if (j < a.Lk) {
-        kreg[i] = *(const uint4*)(kb + j * kv_rs + sc * 8);
-        vreg[i] = *(const uint4*)(vb + j * kv_rs + sc * 8);
-      } else {
-        kreg[i] = make_uint4(0, 0, 0, 0);
-        vreg[i] = make_uint4(0, 0, 0, 0);
-      }
+      kreg[i] = buf_load16(kr, so + i * so_step);
+      vreg[i] = buf_load16(vr, so + i * so_step);
     }
   };
   auto sstore = [&](int stage) {
@@ -153,8 +211,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   f32x16 oacc[C::DB];
 #pragma unroll
   for (int d = 0; d < C::DB; ++d) oacc[d] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
-  const float sl2 = a.scale_log2;
+  float m_ref = -INFINITY;  // exponent base of this row (base-2 units)
+  float l_run = 0.f;        // this lane's share of the row sum
 
   if (t_lo < t_hi) {
     gload(t_lo);
@@ -167,7 +225,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     if (t + 1 < t_hi) gload(t + 1);
     const int jt = t * C::BN;
 
-    // Can any row of this wave see a key of the tile?  Does every row see all?
+    // Wave-uniform tile class: skip (no row of the wave sees a key), full (all
+    // rows see all keys), or masked (straddles a mask edge or the key end).
     bool any = wave_live;
     if (a.causal && jt > wr_hi + off) any = false;
     if (W >= 0 && jt + C::BN - 1 < wr_lo + off - W) any = false;
@@ -177,79 +236,87 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
                       (W < 0 || a.causal || jt + C::BN - 1 <= wr_lo + off + W);
 
     if (any) {
-      const E* ks = smem + stage * 2 * C::TILE;
-      const E* vs = ks + C::TILE;
+      const E* st = smem + stage * 2 * C::TILE;
 
-      // S^T = K Q^T for the tile's two 32-key halves.
+      // S^T = K Q^T for the tile's two 32-key halves (raw scores, fp32).
       f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
       for (int s = 0; s < C::KSTEPS; ++s) {
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
-          const int r = kh * 32 + l32;
-          const V8 kf = *(const V8*)(ks + r * D + (((2 * s + hh) ^ k_swz<D>(r)) << 3));
+          const V8 kf = *(const V8*)(st + koff[s] + kh * 32 * D);
           sacc[kh] = TT::mfma32(kf, qf[s], sacc[kh]);
         }
       }
 
-      // Scale to base 2, mask, running maximum (lane and lane^32 share a row).
-      float mx = -INFINITY;
+      if (!full) {  // element-wise mask, only on edge tiles
+        // Keys row qi may see, relative to this lane's first key of the tile:
+        // key (kh*32 + 8*(r/4) + r%4) is visible iff it lies in [lo, hi].
+        const int base = jt + 4 * hh;
+        const int lo = jlo_row - base, hi = jhi_row - base;
+        const uint32_t span = (uint32_t)(hi - lo);
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
+        for (int kh = 0; kh < 2; ++kh) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = sacc[kh][r] * sl2;
-          if (!full) {
-            const int j = jt + kh * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            const int dj = j - (qi + off);
-            bool ok = j < a.Lk;
-            if (a.causal) ok = ok && dj <= 0;
-            if (W >= 0) ok = ok && dj >= -W && (a.causal || dj <= W);
-            x = ok ? x : -INFINITY;
+          for (int r = 0; r < 16; ++r) {
+            const int rel = kh * 32 + 8 * (r >> 2) + (r & 3);
+            const bool ok = hi >= lo && (uint32_t)(rel - lo) <= span;
+            sacc[kh][r] = ok ? sacc[kh][r] : -INFINITY;
           }
-          sacc[kh][r] = x;
-          mx = fmaxf(mx, x);
         }
       }
-      mx = wave_xor_max(mx, 32);
-      const float m_new = fmaxf(m_run, mx);
-      const float base = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - base);
 
-      // P = 2^(x - m), row sums, and P as the B operand of O^T += V^T P^T.
-      V8 pf[4];
+      // Row maximum of the raw scores (lane and lane^32 share a row).
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kh][r]);
+      mx = max_xor32(mx);
+      const float m_new = mx * sl2;  // sl2 > 0 keeps the order; -inf stays -inf
+
+      // Move the exponent base only when the maximum has grown by more than
+      // the threshold somewhere in the wave; rescale those rows.
+      const bool need = m_new > m_ref + kRescaleThreshold;
+      if (__any(need)) {
+        if (need) {
+          const float alpha = fast_exp2(m_ref - m_new);
+          m_ref = m_new;
+          l_run *= alpha;
+#pragma unroll
+          for (int d = 0; d < C::DB; ++d) oacc[d] *= alpha;
+        }
+      }
+      const float nb = (m_ref == -INFINITY) ? 0.f : -m_ref;
+
+      // P = 2^(s*scale*log2e - base), row sums, packed as the B operand of
+      // O^T += V^T P^T.
+      uint32_t pw[4][4];
       float rs = 0.f;
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(sacc[kh][r] - base);
-          rs += p;
-          pf[2 * kh + (r >> 3)][r & 7] = TT::cvt(p);
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = fast_exp2(__builtin_fmaf(sacc[kh][r], sl2, nb));
+          const float p1 = fast_exp2(__builtin_fmaf(sacc[kh][r + 1], sl2, nb));
+          rs += p0 + p1;
+          pw[2 * kh + (r >> 3)][(r & 7) >> 1] = pack2<TT>(p0, p1);
         }
       }
-      l_run = l_run * alpha + rs;
-      m_run = m_new;
-#pragma unroll
-      for (int d = 0; d < C::DB; ++d) oacc[d] *= alpha;
+      l_run += rs;
 
       // O^T += V^T P^T, 16 keys per MFMA k-step.  Key order inside a step is
       // the one the S^T accumulator hands out: operand index 8*hh + e is key
       // 16*s + 8*(e/4) + 4*hh + e%4.  The two transposed reads fetch exactly
       // those V rows for column d = 32*db + 16*(group&1) + (lane&15).
-      const int j16 = lane & 15, grp = lane >> 4;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const int r0 = 16 * s + 4 * hh + (j16 >> 2);
-        const int r1 = r0 + 8;
+        const V8 pf = __builtin_bit_cast(V8, make_uint4(pw[s][0], pw[s][1], pw[s][2], pw[s][3]));
 #pragma unroll
         for (int d = 0; d < C::DB; ++d) {
-          const int col = 32 * d + 16 * (grp & 1) + 4 * (j16 & 3);
-          const int ch = col >> 3, hf = (col >> 2) & 1;
-          const E* p0 = vs + r0 * D + (((ch ^ v_swz<D>(r0)) << 3) + 4 * hf);
-          const E* p1 = vs + r1 * D + (((ch ^ v_swz<D>(r1)) << 3) + 4 * hf);
-          const V8 vf = cat4<V4, V8>(TT::read_tr(p0), TT::read_tr(p1));
-          oacc[d] = TT::mfma32(vf, pf[s], oacc[d]);
+          const E* p0 = st + voff[d] + 16 * s * D;
+          const V8 vf = cat4<V4, V8>(TT::read_tr(p0), TT::read_tr(p0 + 8 * D));
+          oacc[d] = TT::mfma32(vf, pf, oacc[d]);
         }
       }
     }
@@ -259,7 +326,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   }
 
   // ---- epilogue: normalise, store O in the input type, and the log-sum-exp
-  const float lt = wave_xor_sum(l_run, 32);
+  const float lt = sum_xor32(l_run);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (qi < a.Lq) {
     E* orow = (E*)a.o + ((size_t)((size_t)b * a.Lq + qi) * a.Hq + hq) * D;
@@ -267,14 +334,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     for (int d = 0; d < C::DB; ++d) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        typename TT::vec4 ov;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ov[e] = TT::cvt(oacc[d][4 * q4 + e] * inv);
-        *(typename TT::vec4*)(orow + 32 * d + 8 * q4 + 4 * hh) = ov;
+        const uint2 w = make_uint2(pack2<TT>(oacc[d][4 * q4] * inv, oacc[d][4 * q4 + 1] * inv),
+                                   pack2<TT>(oacc[d][4 * q4 + 2] * inv, oacc[d][4 * q4 + 3] * inv));
+        *(uint2*)(orow + 32 * d + 8 * q4 + 4 * hh) = w;
       }
     }
     if (a.lse != nullptr && hh == 0)
-      a.lse[((size_t)b * a.Hq + hq) * a.Lq + qi] = lt > 0.f ? (m_run + log2f(lt)) * kLn2 : -INFINITY;
+      a.lse[((size_t)b * a.Hq + hq) * a.Lq + qi] = lt > 0.f ? (m_ref + log2f(lt)) * kLn2 : -INFINITY;
   }
 }
 
