@@ -74,6 +74,17 @@ __device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
 
+// Direct global->LDS load: each of the 64 lanes fetches 16 bytes at
+// byte_off inside the resource and the wave writes them to 1 KiB of LDS
+// starting at lds_dst (lane i lands at lds_dst + 16*i).  Out-of-range lanes
+// write zeros.  Completion is tracked by vmcnt (see wait_vmem()).
+__device__ __forceinline__ void buf_load16_lds(rsrc_t r, uint32_t byte_off, void* lds_dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_dst, 16, byte_off, 0,
+                                           0, 0);
+}
+// s_waitcnt vmcnt(0): every vector-memory load of this wave has landed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 template <typename V4, typename V8>
 __device__ __forceinline__ V8 cat4(V4 lo, V4 hi) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);

@@ -97,10 +97,14 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   using E = typename TT::elem;
   using V8 = typename TT::vec8;
   using V4 = typename TT::vec4;
-  __shared__ __attribute__((aligned(16))) E smem[2 * 2 * C::TILE];
+  // [K tile 0][K tile 1][V tile 0][V tile 1]; K runs one tile ahead of V.
+  __shared__ __attribute__((aligned(16))) E smem[4 * C::TILE];
+  E* const kbuf = smem;
+  E* const vbuf = smem + 2 * C::TILE;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keep it scalar
   const int hh = lane >> 5, l32 = lane & 31;
   const int j16 = lane & 15, grp = lane >> 4;
 
@@ -160,7 +164,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   const int wr_hi = min(wr_lo + 31, a.Lq - 1);
   const bool wave_live = wr_lo < a.Lq;
 
-  // ---- per-lane LDS element offsets inside a stage (hoisted out of the loop)
+  // ---- per-lane LDS element offsets inside a tile (hoisted out of the loop)
   int koff[C::KSTEPS];  // K operand of k-step s, first 32-key half (+32*D for the second)
 #pragma unroll
   for (int s = 0; s < C::KSTEPS; ++s) koff[s] = l32 * D + (((2 * s + hh) ^ k_swz<D>(l32)) << 3);
@@ -170,41 +174,63 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int d = 0; d < C::DB; ++d) {
       const int col = 32 * d + 16 * (grp & 1) + 4 * (j16 & 3);
-      voff[d] = C::TILE + r * D + ((((col >> 3) ^ v_swz<D>(r)) << 3) + 4 * ((col >> 2) & 1));
+      voff[d] = r * D + ((((col >> 3) ^ v_swz<D>(r)) << 3) + 4 * ((col >> 2) & 1));
     }
   }
 
-  // ---- staging: thread -> (chunk sc, rows sr + i * RPP)
-  const int sc = tid % C::CPR, sr = tid / C::CPR;
-  const size_t kv_rs = (size_t)a.Hkv * D;  // elements between consecutive keys
+  // ---- staging: direct global->LDS loads, 1 KiB (RPI rows) per wave-instruction.
+  // Lane -> row RPI*i + lane/CPR of the tile, physical chunk lane%CPR, which
+  // holds logical chunk (lane%CPR) ^ swizzle(row).
+  constexpr int RPI = 1024 / (D * (int)sizeof(E));  // rows per instruction
+  constexpr int IPW = C::BN / RPI / 4;              // instructions per wave per tile
+  const size_t kv_rs = (size_t)a.Hkv * D;           // elements between consecutive keys
   const E* kb = (const E*)a.k + ((size_t)b * a.Lk * a.Hkv + g) * D;
   const E* vb = (const E*)a.v + ((size_t)b * a.Lk * a.Hkv + g) * D;
-  // Byte offset of this thread's chunk inside a tile (rows sr + i*RPP).
-  const uint32_t so = (uint32_t)(((size_t)sr * kv_rs + sc * 8) * sizeof(E));
-  const uint32_t so_step = (uint32_t)((size_t)C::RPP * kv_rs * sizeof(E));
-  uint4 kreg[C::KPT], vreg[C::KPT];
-  auto gload = [&](int t) {
+  uint32_t ksrc[IPW], vsrc[IPW];
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int r = (wave * IPW + i) * RPI + lane / C::CPR;
+    const int p = lane % C::CPR;
+    ksrc[i] = (uint32_t)(((size_t)r * kv_rs + ((p ^ k_swz<D>(r)) << 3)) * sizeof(E));
+    vsrc[i] = (uint32_t)(((size_t)r * kv_rs + ((p ^ v_swz<D>(r)) << 3)) * sizeof(E));
+  }
+  auto tile_bytes = [&](int t) -> uint32_t {
     // Resources start at the tile's first key and end after key Lk-1, so
-    // rows past the end of the keys load as zeros.
+    // rows past the end of the keys load as zeros; tiles past the range get
+    // an empty resource (the loads then only write zeros to a free buffer).
+    if (t >= t_hi) return 0u;
     const size_t jt = (size_t)t * C::BN;
     const size_t bytes = (((size_t)(a.Lk - jt) - 1) * kv_rs + D) * sizeof(E);
-    const uint32_t nb = bytes > 0x7fffffffu ? 0x7fffffffu : (uint32_t)bytes;
-    const rsrc_t kr = make_rsrc(kb + jt * kv_rs, nb);
-    const rsrc_t vr = make_rsrc(vb + jt * kv_rs, nb);
-#pragma unroll
-    for (int i = 0; i < C::KPT; ++i) {
-      kreg[i] = buf_load16(kr, so + i * so_step);
-      vreg[i] = buf_load16(vr, so + i * so_step);
-    }
+    return bytes > 0x7fffffffu ? 0x7fffffffu : (uint32_t)bytes;
   };
-  auto sstore = [&](int stage) {
-    E* ks = smem + stage * 2 * C::TILE;
-    E* vs = ks + C::TILE;
+  auto load_k = [&](int t, E* dst) {
+    const rsrc_t r = make_rsrc(kb + (size_t)t * C::BN * kv_rs, tile_bytes(t));
 #pragma unroll
-    for (int i = 0; i < C::KPT; ++i) {
-      const int r = sr + i * C::RPP;
-      *(uint4*)(ks + r * D + ((sc ^ k_swz<D>(r)) << 3)) = kreg[i];
-      *(uint4*)(vs + r * D + ((sc ^ v_swz<D>(r)) << 3)) = vreg[i];
+    for (int i = 0; i < IPW; ++i) buf_load16_lds(r, ksrc[i], dst + (wave * IPW + i) * RPI * D);
+  };
+  auto load_v = [&](int t, E* dst) {
+    const rsrc_t r = make_rsrc(vb + (size_t)t * C::BN * kv_rs, tile_bytes(t));
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) buf_load16_lds(r, vsrc[i], dst + (wave * IPW + i) * RPI * D);
+  };
+
+  // Does every row of this wave see every key of tile t?  (Wave-uniform.)
+  auto tile_full = [&](int t) {
+    const int jt = t * C::BN;
+    return (jt + C::BN <= a.Lk) && (!a.causal || jt + C::BN - 1 <= wr_lo + off) &&
+           (W < 0 || jt >= wr_hi + off - W) && (W < 0 || a.causal || jt + C::BN - 1 <= wr_lo + off + W);
+  };
+  // S^T = K Q^T for one tile: two 32-key halves of raw fp32 scores.
+  auto qk = [&](const E* kt, f32x16* sacc) {
+    sacc[0] = f32x16{};
+    sacc[1] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < C::KSTEPS; ++s) {
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        const V8 kf = *(const V8*)(kt + koff[s] + kh * 32 * D);
+        sacc[kh] = TT::mfma32(kf, qf[s], sacc[kh]);
+      }
     }
   };
 
@@ -214,114 +240,149 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   float m_ref = -INFINITY;  // exponent base of this row (base-2 units)
   float l_run = 0.f;        // this lane's share of the row sum
 
+  // P = 2^(s*scale*log2e - base) for the tile in `sc`, its row sums, and
+  // O^T += V^T P^T, 16 keys per MFMA k-step.  Key order inside a step is the
+  // one the S^T accumulator hands out: operand index 8*hh + e is key
+  // 16*s + 8*(e/4) + 4*hh + e%4.  The two transposed reads fetch exactly
+  // those V rows for column d = 32*db + 16*(group&1) + (lane&15).
+  auto softmax_pv = [&](const f32x16* sc, const E* vt, float nb) {
+    uint32_t pw[4][4];
+    float rs = 0.f;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = fast_exp2(__builtin_fmaf(sc[kh][r], sl2, nb));
+        const float p1 = fast_exp2(__builtin_fmaf(sc[kh][r + 1], sl2, nb));
+        rs += p0 + p1;
+        pw[2 * kh + (r >> 3)][(r & 7) >> 1] = pack2<TT>(p0, p1);
+      }
+    }
+    l_run += rs;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const V8 pf = __builtin_bit_cast(V8, make_uint4(pw[s][0], pw[s][1], pw[s][2], pw[s][3]));
+#pragma unroll
+      for (int d = 0; d < C::DB; ++d) {
+        const E* p0 = vt + voff[d] + 16 * s * D;
+        const V8 vf = cat4<V4, V8>(TT::read_tr(p0), TT::read_tr(p0 + 8 * D));
+        oacc[d] = TT::mfma32(vf, pf, oacc[d]);
+      }
+    }
+  };
+
+  f32x16 scur[2];
   if (t_lo < t_hi) {
-    gload(t_lo);
-    sstore(0);
+    load_k(t_lo, kbuf);
+    load_v(t_lo, vbuf);
+    load_k(t_lo + 1, kbuf + C::TILE);
+    wait_vmem();
+    __syncthreads();
+    qk(kbuf, scur);
+    __syncthreads();  // K(t_lo)'s buffer is refilled by the first iteration
   }
-  __syncthreads();
 
   for (int t = t_lo; t < t_hi; ++t) {
-    const int stage = (t - t_lo) & 1;
-    if (t + 1 < t_hi) gload(t + 1);
-    const int jt = t * C::BN;
+    const int i = t - t_lo;
+    // Loads for the next iteration: K(t+2) into the buffer K(t) used, V(t+1)
+    // into the buffer V(t-1) used.  They land while this tile computes.
+    load_k(t + 2, kbuf + (i & 1) * C::TILE);
+    load_v(t + 1, vbuf + ((i + 1) & 1) * C::TILE);
 
-    // Wave-uniform tile class: skip (no row of the wave sees a key), full (all
-    // rows see all keys), or masked (straddles a mask edge or the key end).
-    bool any = wave_live;
-    if (a.causal && jt > wr_hi + off) any = false;
-    if (W >= 0 && jt + C::BN - 1 < wr_lo + off - W) any = false;
-    if (W >= 0 && !a.causal && jt > wr_hi + off + W) any = false;
-    const bool full = (jt + C::BN <= a.Lk) && (!a.causal || jt + C::BN - 1 <= wr_lo + off) &&
-                      (W < 0 || jt >= wr_hi + off - W) &&
-                      (W < 0 || a.causal || jt + C::BN - 1 <= wr_lo + off + W);
-
-    if (any) {
-      const E* st = smem + stage * 2 * C::TILE;
-
-      // S^T = K Q^T for the tile's two 32-key halves (raw scores, fp32).
-      f32x16 sacc[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-      for (int s = 0; s < C::KSTEPS; ++s) {
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-          const V8 kf = *(const V8*)(st + koff[s] + kh * 32 * D);
-          sacc[kh] = TT::mfma32(kf, qf[s], sacc[kh]);
-        }
-      }
-
-      if (!full) {  // element-wise mask, only on edge tiles
-        // Keys row qi may see, relative to this lane's first key of the tile:
-        // key (kh*32 + 8*(r/4) + r%4) is visible iff it lies in [lo, hi].
-        const int base = jt + 4 * hh;
-        const int lo = jlo_row - base, hi = jhi_row - base;
-        const uint32_t span = (uint32_t)(hi - lo);
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int rel = kh * 32 + 8 * (r >> 2) + (r & 3);
-            const bool ok = hi >= lo && (uint32_t)(rel - lo) <= span;
-            sacc[kh][r] = ok ? sacc[kh][r] : -INFINITY;
-          }
-        }
-      }
-
-      // Row maximum of the raw scores (lane and lane^32 share a row).
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kh][r]);
-      mx = max_xor32(mx);
-      const float m_new = mx * sl2;  // sl2 > 0 keeps the order; -inf stays -inf
-
-      // Move the exponent base only when the maximum has grown by more than
-      // the threshold somewhere in the wave; rescale those rows.
-      const bool need = m_new > m_ref + kRescaleThreshold;
-      if (__any(need)) {
-        if (need) {
-          const float alpha = fast_exp2(m_ref - m_new);
-          m_ref = m_new;
-          l_run *= alpha;
-#pragma unroll
-          for (int d = 0; d < C::DB; ++d) oacc[d] *= alpha;
-        }
-      }
-      const float nb = (m_ref == -INFINITY) ? 0.f : -m_ref;
-
-      // P = 2^(s*scale*log2e - base), row sums, packed as the B operand of
-      // O^T += V^T P^T.
-      uint32_t pw[4][4];
-      float rs = 0.f;
+    if (!tile_full(t)) {  // element-wise mask, only on edge tiles
+      // Keys row qi may see, relative to this lane's first key of the tile:
+      // key (kh*32 + 8*(r/4) + r%4) is visible iff it lies in [lo, hi].
+      const int base = t * C::BN + 4 * hh;
+      const int lo = jlo_row - base, hi = jhi_row - base;
+      const uint32_t span = (uint32_t)(hi - lo);
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = fast_exp2(__builtin_fmaf(sacc[kh][r], sl2, nb));
-          const float p1 = fast_exp2(__builtin_fmaf(sacc[kh][r + 1], sl2, nb));
+        for (int r = 0; r < 16; ++r) {
+          const int rel = kh * 32 + 8 * (r >> 2) + (r & 3);
+          const bool ok = hi >= lo && (uint32_t)(rel - lo) <= span;
+          scur[kh][r] = ok ? scur[kh][r] : -INFINITY;
+        }
+      }
+    }
+
+    // Row maximum of the raw scores (lane and lane^32 share a row).
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, scur[kh][r]);
+    mx = max_xor32(mx);
+    const float m_new = mx * sl2;  // sl2 > 0 keeps the order; -inf stays -inf
+
+    // Move the exponent base only when the maximum has grown by more than the
+    // threshold somewhere in the wave; rescale those rows.
+    const bool need = m_new > m_ref + kRescaleThreshold;
+    if (__any(need)) {
+      if (need) {
+        const float alpha = fast_exp2(m_ref - m_new);
+        m_ref = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < C::DB; ++d) oacc[d] *= alpha;
+      }
+    }
+    const float nb = (m_ref == -INFINITY) ? 0.f : -m_ref;
+    const E* vt = vbuf + (i & 1) * C::TILE;
+
+    {
+      // One straight-line block that software-pipelines the next tile's
+      // S^T = K Q^T with this tile's softmax: per k-step, the K operands of
+      // the following step are read, the two MFMAs of this step issue, and a
+      // share of this tile's exponentials, row sums and P packing runs on the
+      // vector ALU while those MFMAs execute.  Then O^T += V^T P^T.  On the
+      // last tile the next-tile product reads a stale buffer and is discarded
+      // (cheaper than a second copy of the block).  sched_barrier keeps the
+      // compiler from regrouping the steps.
+      constexpr int EPS = 32 / C::KSTEPS;  // score elements exponentiated per k-step
+      const E* kt = kbuf + ((i + 1) & 1) * C::TILE;
+      f32x16 snext[2] = {f32x16{}, f32x16{}};
+      uint32_t pw[4][4];
+      float rs = 0.f;
+      V8 kcur0 = *(const V8*)(kt + koff[0]);
+      V8 kcur1 = *(const V8*)(kt + koff[0] + 32 * D);
+#pragma unroll
+      for (int s = 0; s < C::KSTEPS; ++s) {
+        V8 knext0 = kcur0, knext1 = kcur1;
+        if (s + 1 < C::KSTEPS) {
+          knext0 = *(const V8*)(kt + koff[s + 1]);
+          knext1 = *(const V8*)(kt + koff[s + 1] + 32 * D);
+        }
+        snext[0] = TT::mfma32(kcur0, qf[s], snext[0]);
+        snext[1] = TT::mfma32(kcur1, qf[s], snext[1]);
+#pragma unroll
+        for (int e = 0; e < EPS; e += 2) {
+          const int f = s * EPS + e;  // flat element index kh*16 + r
+          const int kh = f >> 4, r = f & 15;
+          const float p0 = fast_exp2(__builtin_fmaf(scur[kh][r], sl2, nb));
+          const float p1 = fast_exp2(__builtin_fmaf(scur[kh][r + 1], sl2, nb));
           rs += p0 + p1;
           pw[2 * kh + (r >> 3)][(r & 7) >> 1] = pack2<TT>(p0, p1);
         }
+        kcur0 = knext0;
+        kcur1 = knext1;
+        __builtin_amdgcn_sched_barrier(0);
       }
       l_run += rs;
-
-      // O^T += V^T P^T, 16 keys per MFMA k-step.  Key order inside a step is
-      // the one the S^T accumulator hands out: operand index 8*hh + e is key
-      // 16*s + 8*(e/4) + 4*hh + e%4.  The two transposed reads fetch exactly
-      // those V rows for column d = 32*db + 16*(group&1) + (lane&15).
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const V8 pf = __builtin_bit_cast(V8, make_uint4(pw[s][0], pw[s][1], pw[s][2], pw[s][3]));
 #pragma unroll
         for (int d = 0; d < C::DB; ++d) {
-          const E* p0 = st + voff[d] + 16 * s * D;
+          const E* p0 = vt + voff[d] + 16 * s * D;
           const V8 vf = cat4<V4, V8>(TT::read_tr(p0), TT::read_tr(p0 + 8 * D));
           oacc[d] = TT::mfma32(vf, pf, oacc[d]);
         }
       }
+      scur[0] = snext[0];
+      scur[1] = snext[1];
     }
-
-    if (t + 1 < t_hi) sstore(stage ^ 1);
+    wait_vmem();
     __syncthreads();
   }
 
