@@ -109,10 +109,11 @@ def test_decode_valid_args_without_gpu_report_device():
 
 def test_workspace_size():
     ws = ta.attn_decode_paged_workspace_size
-    # 256-token chunks: 4096 tokens -> 16 partials of (D outputs + 1 lse) floats
-    assert ws(64, 12, 128, 256, 16) == 64 * 12 * 16 * 129 * 4
-    assert ws(3, 6, 64, 1, 16) == 3 * 6 * 1 * 65 * 4
-    assert ws(3, 6, 64, 17, 16) == 3 * 6 * 2 * 65 * 4
+    # slots = min(2048 ranges, blocks of all sequences) + sequences, each holding
+    # one partial of (D outputs + 1 lse) floats per query head
+    assert ws(64, 12, 128, 256, 16) == (2048 + 64) * 12 * 129 * 4
+    assert ws(3, 6, 64, 1, 16) == (3 + 3) * 6 * 65 * 4
+    assert ws(3, 6, 64, 17, 16) == (51 + 3) * 6 * 65 * 4
     assert ws(0, 12, 128, 256, 16) == 0
     assert ws(4, 12, 100, 256, 16) == 0
     assert ws(4, 12, 128, 256, 32) == 0

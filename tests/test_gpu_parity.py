@@ -292,3 +292,50 @@ def test_paged_matches_dense_forward(gpu_lib):
         o2, l2 = run_fwd(gpu_lib, inp.q[s][None, None], kt, vt, cfg.scale, False, -1)
         assert (o2[0, 0].float() - out[s].float()).abs().max().item() <= 2 * TOL["bf16"]
         assert (l2[0, :, 0] - lse[s]).abs().max().item() <= 2 * LSE_TOL
+
+
+def _paged_case(name, ctx, Hq, Hkv, D, dtype, seed):
+    from workloads import PagedConfig
+    ctx = np.asarray(ctx, dtype=np.int64)
+    cfg = PagedConfig("adhoc", len(ctx), Hq, Hkv, D, dtype, 0, int(max(ctx.max(), 1)), 16, seed)
+    return cfg, paged_inputs(cfg, ctx_lens=ctx)
+
+
+def test_paged_many_tiny_sequences(gpu_lib):
+    """Lengths 0..40: ranges hold several whole sequences (direct output) and
+    sequences split over ranges (merged partials) in one launch."""
+    say("[case] paged many tiny sequences")
+    ctx = np.random.default_rng(16).integers(0, 41, size=300)
+    cfg, inp = _paged_case("tiny", ctx, 8, 2, 64, "bf16", 16)
+    out, lse = run_decode(gpu_lib, inp, cfg.scale)
+    ro, rl = oracle.decode_paged(inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.ctx_lens, 16, cfg.scale)
+    check("paged tiny seqs", out, lse, ro, rl, "bf16")
+
+
+def test_paged_more_sequences_than_one_launch(gpu_lib):
+    """2100 sequences: the call is cut into launches of at most 2048."""
+    say("[case] paged 2100 sequences")
+    ctx = np.random.default_rng(17).integers(1, 50, size=2100)
+    cfg, inp = _paged_case("many", ctx, 4, 2, 64, "fp16", 17)
+    out, lse = run_decode(gpu_lib, inp, cfg.scale)
+    ro, rl = oracle.decode_paged(inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.ctx_lens, 16, cfg.scale)
+    check("paged 2100 seqs", out, lse, ro, rl, "fp16")
+
+
+def test_paged_long_ranges_and_wide_groups(gpu_lib):
+    """256 query heads on one KV head (16 head groups of 16): few ranges per
+    group, each longer than one 64-block window."""
+    say("[case] paged long ranges")
+    ctx = np.array([16400, 5, 20000, 16, 30001], dtype=np.int64)
+    cfg, inp = _paged_case("long", ctx, 256, 1, 128, "bf16", 18)
+    out, lse = run_decode(gpu_lib, inp, cfg.scale)
+    ro, rl = oracle.decode_paged(inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.ctx_lens, 16, cfg.scale)
+    check("paged long ranges", out, lse, ro, rl, "bf16")
+
+
+def test_paged_deterministic_bitwise(gpu_lib):
+    cfg = CONFIGS["paged_decode"]
+    inp = paged_inputs(cfg, seed=19)
+    a, la = run_decode(gpu_lib, inp, cfg.scale)
+    b, lb = run_decode(gpu_lib, inp, cfg.scale)
+    assert torch.equal(a, b) and torch.equal(la, lb)

@@ -2,6 +2,7 @@
 // Declarations and the full contract are in include/attn.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstring>
@@ -16,10 +17,12 @@ namespace {
 constexpr int kMaxDevices = 64;
 // 0 = not checked yet, 1 = gfx950, 2 = something else.
 std::atomic<int> g_arch_ok[kMaxDevices];
+std::atomic<int> g_cu_count[kMaxDevices];
 
-// The device current on this thread must be gfx950 (CDNA4).  The result is
-// cached per device id; racing first calls just both query.
-int check_device() {
+// The device current on this thread must be gfx950 (CDNA4).  The result and
+// the device's CU count are cached per device id; racing first calls just
+// both query.
+int check_device(int* cus = nullptr) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return ATTN_ERR_DEVICE;
   if (dev >= kMaxDevices) return ATTN_ERR_DEVICE;
@@ -27,9 +30,11 @@ int check_device() {
   if (st == 0) {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ATTN_ERR_DEVICE;
+    g_cu_count[dev].store(prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1, std::memory_order_relaxed);
     st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
     g_arch_ok[dev].store(st, std::memory_order_release);
   }
+  if (cus) *cus = g_cu_count[dev].load(std::memory_order_relaxed);
   return st == 1 ? ATTN_OK : ATTN_ERR_DEVICE;
 }
 
@@ -50,9 +55,11 @@ bool prod_ok(long long a, long long b, long long c, long long d) {
   return true;
 }
 
-int decode_n_split(int max_blocks_per_seq, int block_size) {
-  const long long toks = (long long)max_blocks_per_seq * block_size;
-  return (int)((toks + attn::kDecodeChunk - 1) / attn::kDecodeChunk);
+// Sequences per decode launch: at most kDecodeMaxSeqsPerLaunch, and few
+// enough that their block count fits the kernels' 32-bit counters.
+int decode_seqs_per_launch(int max_blocks_per_seq) {
+  const long long by_blocks = 0x7fffffffLL / max_blocks_per_seq;
+  return (int)std::min<long long>(attn::kDecodeMaxSeqsPerLaunch, std::max<long long>(1, by_blocks));
 }
 
 }  // namespace
@@ -102,12 +109,21 @@ ATTN_API int attn_fwd(const void* q, const void* k, const void* v, void* out, fl
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+// Workspace slots of one decode launch: one per (range, sequence) pair that
+// can leave a partial, indexed range + sequence, so fewer than
+// ranges + sequences; ranges never outnumber the launch's cache blocks.
+static long long decode_slots(int num_seqs, int max_blocks_per_seq) {
+  const long long n = std::min(num_seqs, decode_seqs_per_launch(max_blocks_per_seq));
+  return std::min<long long>(attn::kDecodeMaxStreams, n * max_blocks_per_seq) + n;
+}
+
 ATTN_API size_t attn_decode_paged_workspace_size(int num_seqs, int Hq, int D, int max_blocks_per_seq,
                                                  int block_size) {
   if (num_seqs <= 0 || Hq <= 0 || max_blocks_per_seq <= 0 || block_size != 16 || !supported_d(D)) return 0;
-  const long long n_split = decode_n_split(max_blocks_per_seq, block_size);
-  if (!prod_ok(num_seqs, Hq, n_split, D + 1)) return 0;
-  return (size_t)num_seqs * Hq * n_split * (D + 1) * sizeof(float);
+  // One partial (D outputs + a log2-sum-exp) per query head and slot.
+  const long long slots = decode_slots(num_seqs, max_blocks_per_seq);
+  if (!prod_ok(slots, Hq, D + 1, (long long)sizeof(float))) return 0;
+  return (size_t)slots * Hq * (D + 1) * sizeof(float);
 }
 
 ATTN_API int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
@@ -133,22 +149,41 @@ ATTN_API int attn_decode_paged(const void* q, const void* k_cache, const void* v
   const size_t need = attn_decode_paged_workspace_size(num_seqs, Hq, D, max_blocks_per_seq, block_size);
   if (need == 0 || !workspace || workspace_bytes < need || !aligned(workspace, 16)) return ATTN_ERR_WORKSPACE;
   const int group = Hq / Hkv;
-  const int n_split = decode_n_split(max_blocks_per_seq, block_size);
   const int n_hgroups = (group + 15) / 16;
-  if ((long long)num_seqs * Hkv * n_hgroups * n_split > 0x7fffffffLL) return ATTN_ERR_SHAPE;
-  const int dev = check_device();
+  int cus = 0;
+  const int dev = check_device(&cus);
   if (dev != ATTN_OK) return dev;
 
+  const int per_launch = decode_seqs_per_launch(max_blocks_per_seq);
+  // Ranges per (KV head, head group): enough waves to give every CU one
+  // resident work-group, never more ranges than blocks.
+  long long streams = (long long)cus * attn::kDecodeWavesPerCU / ((long long)Hkv * n_hgroups);
+  streams = std::min<long long>(streams, (long long)std::min(num_seqs, per_launch) * max_blocks_per_seq);
+  streams = std::max<long long>(1, std::min<long long>(streams, attn::kDecodeMaxStreams));
+  const size_t esz = 2;  // fp16 / bf16
+  const size_t slots = (size_t)decode_slots(num_seqs, max_blocks_per_seq);
+
   attn::DecArgs a;
-  a.q = q; a.k_cache = k_cache; a.v_cache = v_cache;
-  a.block_table = block_table; a.ctx_lens = ctx_lens;
-  a.o = out; a.lse = lse;
+  a.k_cache = k_cache; a.v_cache = v_cache;
   a.ws_o = (float*)workspace;
-  a.ws_lse = (float*)workspace + (size_t)num_seqs * Hq * n_split * D;
-  a.num_seqs = num_seqs; a.Hq = Hq; a.Hkv = Hkv; a.group = group;
+  a.ws_lse = (float*)workspace + slots * Hq * D;
+  a.Hq = Hq; a.Hkv = Hkv; a.group = group;
   a.max_blocks_per_seq = max_blocks_per_seq; a.num_blocks = num_blocks;
-  a.n_split = n_split; a.n_hgroups = n_hgroups;
+  a.n_hgroups = n_hgroups;
+  a.streams = (int)streams;
   a.scale_log2 = scale * attn::kLog2e;
-  hipError_t e = attn::launch_decode(a, D, dtype, (hipStream_t)stream);
-  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+  // Launches of successive sequence batches share the workspace; the stream
+  // orders them.
+  for (int s0 = 0; s0 < num_seqs; s0 += per_launch) {
+    const int n = std::min(per_launch, num_seqs - s0);
+    a.q = (const char*)q + (size_t)s0 * Hq * D * esz;
+    a.o = (char*)out + (size_t)s0 * Hq * D * esz;
+    a.lse = lse ? lse + (size_t)s0 * Hq : nullptr;
+    a.block_table = block_table + (size_t)s0 * max_blocks_per_seq;
+    a.ctx_lens = ctx_lens + s0;
+    a.num_seqs = n;
+    hipError_t e = attn::launch_decode(a, D, dtype, (hipStream_t)stream);
+    if (e != hipSuccess) return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
 }

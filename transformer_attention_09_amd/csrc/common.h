@@ -6,6 +6,8 @@
 //    C[8*(r/4) + 4*(l/32) + r%4][l%32].
 //  v_mfma_f32_16x16x32_{bf16,f16}: lane l holds A[l%16][8*(l/16)+e] and
 //    B[8*(l/16)+e][l%16]; register r of lane l is C[4*(l/16) + r][l%16].
+//  v_mfma_f32_16x16x16_{bf16,f16}: as above with 4 elements per lane:
+//    A[l%16][4*(l/16)+e], B[4*(l/16)+e][l%16] (e = 0..3); same C layout.
 //  ds_read_b64_tr_b16: inside each group of 16 lanes, lane i receives
 //    element i%4 of the 8-byte chunk addressed by group lane 4*e + i/4, for
 //    e = 0..3.  Pointing group lane j at row (r0 + j/4), columns
@@ -24,6 +26,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
@@ -37,6 +40,10 @@ struct BF16 {
   }
   static __device__ __forceinline__ f32x4 mfma16(vec8 a, vec8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma16k16(vec4 a, vec4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c,
+                                                     0, 0, 0);
   }
   static __device__ __forceinline__ vec4 read_tr(const void* lds) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(vec4, lds));
@@ -55,6 +62,9 @@ struct F16 {
   static __device__ __forceinline__ f32x4 mfma16(vec8 a, vec8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
   }
+  static __device__ __forceinline__ f32x4 mfma16k16(vec4 a, vec4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+  }
   static __device__ __forceinline__ vec4 read_tr(const void* lds) {
     typedef __fp16 h4 __attribute__((ext_vector_type(4)));
     return __builtin_bit_cast(vec4, __builtin_amdgcn_ds_read_tr16_b64_v4f16(LDS_PTR(h4, lds)));
@@ -72,6 +82,106 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 }
 __device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+// Range-checked stores: a store outside [0, bytes) of its resource is dropped,
+// so a resource of size 0 turns a store into a no-op without a branch.
+typedef unsigned u32x4_t __attribute__((vector_size(16)));
+typedef unsigned u32x2_t __attribute__((vector_size(8)));
+__device__ __forceinline__ void buf_store16(rsrc_t r, uint32_t byte_off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, byte_off, 0, 0);
+}
+__device__ __forceinline__ void buf_store8(rsrc_t r, uint32_t byte_off, u32x2_t v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, byte_off, 0, 0);
+}
+__device__ __forceinline__ void buf_store4(rsrc_t r, uint32_t byte_off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, byte_off, 0, 0);
+}
+
+// Memory reads written as inline assembly.  The compiler does not see what
+// they read, so it adds no memory-counter wait for direct-to-LDS loads in
+// flight; the caller places that wait (wait_vm).  Each block issues its reads
+// and waits for them before it ends, so its outputs are complete when the
+// statement completes.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+// s_waitcnt vmcnt(N): at most N vector-memory operations of this wave remain
+// outstanding (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
+}
+// Four 16-byte reads (ds_read_b128).
+__device__ __forceinline__ void lds_read16_x4(u32x4_t (&r)[4], const uint32_t (&addr)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+      : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3])
+      : "memory");
+}
+__device__ __forceinline__ void lds_read16_x2(u32x4_t (&r)[2], const uint32_t (&addr)[2]) {
+  asm volatile(
+      "ds_read_b128 %0, %2\n\t"
+      "ds_read_b128 %1, %3\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1])
+      : "v"(addr[0]), "v"(addr[1])
+      : "memory");
+}
+// Transposed reads (ds_read_b64_tr_b16, lane layout at the top of this file).
+__device__ __forceinline__ void lds_read_tr8_x8(u32x2_t (&r)[8], const uint32_t (&addr)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %9\n\t"
+      "ds_read_b64_tr_b16 %2, %10\n\t"
+      "ds_read_b64_tr_b16 %3, %11\n\t"
+      "ds_read_b64_tr_b16 %4, %12\n\t"
+      "ds_read_b64_tr_b16 %5, %13\n\t"
+      "ds_read_b64_tr_b16 %6, %14\n\t"
+      "ds_read_b64_tr_b16 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
+        "=&v"(r[7])
+      : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "v"(addr[4]), "v"(addr[5]), "v"(addr[6]),
+        "v"(addr[7])
+      : "memory");
+}
+// Four (two) 16-byte buffer loads, then s_waitcnt vmcnt(0): this also waits
+// for every earlier vector-memory operation of the wave.
+__device__ __forceinline__ void buf_load16_x4_sync(u32x4_t (&r)[4], rsrc_t rs, const uint32_t (&off)[4]) {
+  asm volatile(
+      "buffer_load_dwordx4 %0, %4, %8, 0 offen\n\t"
+      "buffer_load_dwordx4 %1, %5, %8, 0 offen\n\t"
+      "buffer_load_dwordx4 %2, %6, %8, 0 offen\n\t"
+      "buffer_load_dwordx4 %3, %7, %8, 0 offen\n\t"
+      "s_waitcnt vmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+      : "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "s"(rs)
+      : "memory");
+}
+__device__ __forceinline__ void buf_load16_x2_sync(u32x4_t (&r)[2], rsrc_t rs, const uint32_t (&off)[2]) {
+  asm volatile(
+      "buffer_load_dwordx4 %0, %2, %4, 0 offen\n\t"
+      "buffer_load_dwordx4 %1, %3, %4, 0 offen\n\t"
+      "s_waitcnt vmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1])
+      : "v"(off[0]), "v"(off[1]), "s"(rs)
+      : "memory");
+}
+__device__ __forceinline__ void lds_read_tr8_x4(u32x2_t (&r)[4], const uint32_t (&addr)[4]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4\n\t"
+      "ds_read_b64_tr_b16 %1, %5\n\t"
+      "ds_read_b64_tr_b16 %2, %6\n\t"
+      "ds_read_b64_tr_b16 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+      : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3])
+      : "memory");
 }
 
 // Direct global->LDS load: each of the 64 lanes fetches 16 bytes at

@@ -5,28 +5,34 @@
 // paging leaves the set of attended elements unchanged).
 //
 // The work is bound by HBM bandwidth: every K/V byte of every context is read
-// once per KV head and used by the Hq/Hkv query heads of its group.  To give
-// the 256 CUs enough independent streams, each sequence's context is split
-// into chunks of 256 tokens ("split-K"):
+// once and used by the Hq/Hkv query heads of its KV head.  The kernel is
+// shaped so that every CU streams the same number of bytes, with several
+// cache blocks in flight per wave, and so that the two halves of a block that
+// belong to different KV heads are read at the same time:
 //
-//   decode_split_kernel: one work-group = (sequence, KV head, query-head group
-//     of up to 16, chunk).  Each of its 4 waves takes 4 cache blocks (64
-//     tokens): it resolves the block ids, issues all K and V loads at once
-//     (64 B per lane per block and tensor, coalesced along D), computes
-//     S^T = K Q^T with 16x16x32 MFMA (tokens x query heads), a per-wave
-//     softmax in base 2, stages its V blocks in LDS and accumulates
-//     O^T = V^T P^T with MFMA, fetching V^T with the LDS transpose read.  The
-//     4 wave partials are merged in LDS with the online-softmax rescaling and
-//     one normalised partial (o, log2-sum-exp) per chunk goes to the
-//     workspace.
-//   decode_combine_kernel: merges the chunk partials of each (sequence, query
-//     head): M = max_c lse_c, w_c = 2^(lse_c - M), out = sum w_c o_c / sum w_c.
-//     This is the same rescaling identity the online softmax uses («Самовнимание,
-//     ядра CUDA и FlashAttention», section 3), applied across chunks.
+//   decode_split_kernel: the cache blocks of all sequences, in sequence order,
+//     form one list of NB blocks.  Each (KV head, query-head group of <= 16)
+//     cuts it into `streams` equal contiguous ranges; one wave owns one range
+//     (a work-group's 4 waves are neighbouring ranges/KV heads).  The unit of
+//     work is one 16-token block of one KV head: its K and V tiles go
+//     global->LDS with direct-to-LDS loads (range-checked, so slots past the
+//     sequence's length arrive as zeros), DEPTH units ahead of the one being
+//     computed.  Per unit, S^T = K Q^T (16 tokens x 16 query heads) on a
+//     16x16x32 MFMA, an online softmax in base 2 over the tokens, and
+//     O^T += V^T P^T on 16x16x16 MFMAs with V^T fetched by the LDS transpose
+//     read and P^T taken straight from the S^T accumulators.  At the end of a
+//     sequence's run inside the range, the wave writes either the final
+//     output (the range holds the whole sequence) or a partial (normalised
+//     output and log2-sum-exp) into workspace slot (range + sequence).
+//   decode_combine_kernel: merges the partials of each split sequence:
+//     M = max_c lse_c, w_c = 2^(lse_c - M), out = sum w_c o_c / sum w_c.  This
+//     is the online-softmax rescaling («Самовнимание, ядра CUDA и
+//     FlashAttention», section 3) applied across ranges.
 //
-// Slots past a sequence's length are masked to -inf before the softmax and
-// their V rows are zeroed in LDS, so stale or non-finite cache contents never
-// reach the result.
+// The LDS reads of a unit are inline assembly preceded by an explicit wait
+// for that unit's own loads only (the compiler cannot tell which in-flight
+// direct-to-LDS load a read depends on and would otherwise wait for all of
+// them), so DEPTH-1 units stay in flight while one computes.
 #include "common.h"
 #include "internal.h"
 
@@ -34,240 +40,430 @@ namespace attn {
 
 template <int D>
 struct DecCfg {
-  static constexpr int NT = 256, WAVES = 4;
-  static constexpr int BS = 16;                       // tokens per cache block
-  static constexpr int BPW = 4;                       // cache blocks per wave
-  static constexpr int CHUNK = WAVES * BPW * BS;      // tokens per work-group
-  static constexpr int DSTEPS = D / 32;               // k-steps of S^T
-  static constexpr int DB = D / 16;                   // 16-row blocks of O^T
-  static constexpr int LPT = D / 4;                   // elements per lane per token row
-  static constexpr int WAVE_ELEMS = BPW * BS * D;     // LDS elements of one wave's V
-  static_assert(CHUNK == kDecodeChunk, "chunk size mismatch");
+  static constexpr int BS = 16;           // tokens per cache block
+  static constexpr int WAVES = 4;         // ranges per work-group
+  static constexpr int DEPTH = 4;         // units in flight per wave
+  static constexpr int ROW = D * 2;       // bytes of one token of one KV head
+  static constexpr int TILE = BS * D;     // elements of one K or V tile
+  static constexpr int CPR = ROW / 16;    // 16-byte chunks per row
+  static constexpr int LPI = 1024 / ROW;  // rows per 1 KiB direct-to-LDS load
+  static constexpr int IPT = BS / LPI;    // loads per tile
+  static constexpr int KS = D / 32;       // k-steps of S^T = K Q^T (16x16x32)
+  static constexpr int DB = D / 16;       // 16-row blocks of O^T (16x16x16)
+  static constexpr int OPS = 2 * IPT;     // vector-memory loads issued per unit
+  static_assert(DEPTH == 4, "the unit loop below is unrolled for 4 slots");
 };
 
-// Chunk swizzle of V rows in LDS.  A transposed read covers 16 rows (one per
-// slot) x 2 adjacent chunks per instruction; rows r..r+7 land on distinct
-// chunk pairs.
+// Chunk swizzles.  K: the 16 lanes of a K-operand read fetch one chunk from
+// each of 16 rows; row t holds logical chunk c at c ^ (t mod CPR), so they hit
+// distinct chunks.  V: a transposed read fetches a chunk pair from 16 rows;
+// row t shifts pairs by 2*t mod CPR, so 8 consecutive rows use distinct pairs.
 template <int D>
-__device__ __forceinline__ int dv_swz(int r) {
-  if constexpr (D == 128) return (r & 7) << 1;
-  else return (r & 3) << 1;
-}
+__device__ __forceinline__ int dk_swz(int t) { return t & (DecCfg<D>::CPR - 1); }
+template <int D>
+__device__ __forceinline__ int dv_swz(int t) { return (2 * t) & (DecCfg<D>::CPR - 1); }
+
+// The running maximum used as the exponent base only moves when a head's new
+// maximum exceeds it by more than this (base-2 units); the output rescale is
+// then skipped on most units.
+constexpr float kDecRescaleThreshold = 8.0f;
+
+template <int J>
+struct Slot {
+  static constexpr int value = J;
+};
 
 template <typename TT, int D>
-__global__ __launch_bounds__(256, 2) void decode_split_kernel(DecArgs a) {
+__global__ __launch_bounds__(256, 1) void decode_split_kernel(DecArgs a) {
   using C = DecCfg<D>;
   using E = typename TT::elem;
   using V8 = typename TT::vec8;
   using V4 = typename TT::vec4;
-  __shared__ __attribute__((aligned(16))) E sv[C::WAVES * C::WAVE_ELEMS];
-  __shared__ float sm_m[C::WAVES][16], sm_l[C::WAVES][16];
+  __shared__ __attribute__((aligned(16))) E kb0[C::WAVES * C::TILE];
+  __shared__ __attribute__((aligned(16))) E kb1[C::WAVES * C::TILE];
+  __shared__ __attribute__((aligned(16))) E kb2[C::WAVES * C::TILE];
+  __shared__ __attribute__((aligned(16))) E kb3[C::WAVES * C::TILE];
+  __shared__ __attribute__((aligned(16))) E vb0[C::WAVES * C::TILE];
+  __shared__ __attribute__((aligned(16))) E vb1[C::WAVES * C::TILE];
+  __shared__ __attribute__((aligned(16))) E vb2[C::WAVES * C::TILE];
+  __shared__ __attribute__((aligned(16))) E vb3[C::WAVES * C::TILE];
+  __shared__ int pref[kDecodeMaxSeqsPerLaunch];  // inclusive prefix of per-sequence block counts
+  __shared__ int wtot[C::WAVES];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l16 = lane & 15, g4 = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = lane >> 4, c16 = lane & 15;
+  const int ns = a.num_seqs;
+  const int cap = a.max_blocks_per_seq * C::BS;
 
-  int id = blockIdx.x;
-  const int c = id % a.n_split;
-  id /= a.n_split;
-  const int hg = id % a.n_hgroups;
-  id /= a.n_hgroups;
-  const int g = id % a.Hkv;
-  const int s = id / a.Hkv;
-
-  const int ctx = min(max(a.ctx_lens[s], 0), a.max_blocks_per_seq * C::BS);
-  if (c * C::CHUNK >= ctx) return;  // uniform over the work-group: no barrier reached
-
-  // Query heads of this work-group: hq = g*group + hg*16 + (lane % 16).
-  const int hj = hg * 16 + l16;
-  const bool head_ok = hj < a.group;
-  const int hq = g * a.group + hj;
-
-  // Q operand (B of S^T): lane holds head l16, d = LPT*g4 + 8*ds + e.
-  V8 qf[C::DSTEPS];
-  {
-    const E* qrow = (const E*)a.q + ((size_t)s * a.Hq + hq) * D + C::LPT * g4;
+  // ---- 1. block counts of all sequences -> inclusive prefix in LDS.
+  // Thread t takes the run of up to 8 sequences [8t, 8t+8).
+  int nbv[8];
+  int local = 0;
+  const int s_beg = tid * 8;
 #pragma unroll
-    for (int ds = 0; ds < C::DSTEPS; ++ds) qf[ds] = head_ok ? *(const V8*)(qrow + 8 * ds) : V8{};
+  for (int i = 0; i < 8; ++i) {
+    const int s = s_beg + i;
+    const int c = s < ns ? min(max(a.ctx_lens[s], 0), cap) : 0;
+    nbv[i] = (c + C::BS - 1) / C::BS;
+    local += nbv[i];
   }
-
-  // This wave's cache blocks: logical lb = chunk*16 + wave*4 + i.
-  const int lb0 = c * (C::CHUNK / C::BS) + wave * C::BPW;
-  int pb[C::BPW];
-  bool bvalid[C::BPW];
+  int x = local;
 #pragma unroll
-  for (int i = 0; i < C::BPW; ++i) {
-    const int lb = lb0 + i;
-    bvalid[i] = lb * C::BS < ctx;
-    int p = bvalid[i] ? a.block_table[(size_t)s * a.max_blocks_per_seq + lb] : 0;
-    pb[i] = min(max(p, 0), a.num_blocks - 1);
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
   }
-
-  // Issue every K and V load of the wave: lane -> (slot l16, d-range LPT*g4).
-  const size_t tok_rs = (size_t)a.Hkv * D;     // elements between slots
-  const size_t blk_rs = (size_t)C::BS * tok_rs;  // elements between blocks
-  uint4 kr[C::BPW][C::DSTEPS], vr[C::BPW][C::DSTEPS];
-#pragma unroll
-  for (int i = 0; i < C::BPW; ++i) {
-    const size_t o = pb[i] * blk_rs + l16 * tok_rs + (size_t)g * D + C::LPT * g4;
-#pragma unroll
-    for (int ds = 0; ds < C::DSTEPS; ++ds) {
-      if (bvalid[i]) {
-        kr[i][ds] = *(const uint4*)((const E*)a.k_cache + o + 8 * ds);
-        vr[i][ds] = *(const uint4*)((const E*)a.v_cache + o + 8 * ds);
-      } else {
-        kr[i][ds] = make_uint4(0, 0, 0, 0);
-        vr[i][ds] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  }
-
-  // S^T = K Q^T per block: register r of lane = (slot 4*g4 + r, head l16).
-  f32x4 sacc[C::BPW];
-  float mx = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < C::BPW; ++i) {
-    sacc[i] = f32x4{};
-#pragma unroll
-    for (int ds = 0; ds < C::DSTEPS; ++ds) {
-      const V8 kf = __builtin_bit_cast(V8, kr[i][ds]);
-      sacc[i] = TT::mfma16(kf, qf[ds], sacc[i]);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int pos = (lb0 + i) * C::BS + 4 * g4 + r;
-      const float x = pos < ctx ? sacc[i][r] * a.scale_log2 : -INFINITY;
-      sacc[i][r] = x;
-      mx = fmaxf(mx, x);
-    }
-  }
-  mx = max_xor16(mx);
-  mx = max_xor32(mx);
-  const float base = (mx == -INFINITY) ? 0.f : mx;
-
-  // P (B operand of O^T = V^T P^T): k index 8*g4 + e is
-  // (block 2*ks + e/4, slot 4*g4 + e%4).
-  V8 pf[C::BPW / 2];
-  float lsum = 0.f;
-#pragma unroll
-  for (int i = 0; i < C::BPW; ++i) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float p = fast_exp2(sacc[i][r] - base);
-      lsum += p;
-      pf[i >> 1][4 * (i & 1) + r] = TT::cvt(p);
-    }
-  }
-  lsum = sum_xor16(lsum);
-  lsum = sum_xor32(lsum);
-
-  // Stage this wave's V blocks in LDS ([block][slot][d], chunk-swizzled);
-  // slots past the context are written as zeros.
-  E* wv = sv + wave * C::WAVE_ELEMS;
-#pragma unroll
-  for (int i = 0; i < C::BPW; ++i) {
-    const int row = i * C::BS + l16;
-    const bool live = (lb0 + i) * C::BS + l16 < ctx;
-#pragma unroll
-    for (int ds = 0; ds < C::DSTEPS; ++ds) {
-      const int ch = (C::LPT / 8) * g4 + ds;
-      *(uint4*)(wv + row * D + ((ch ^ dv_swz<D>(row)) << 3)) = live ? vr[i][ds] : make_uint4(0, 0, 0, 0);
-    }
-  }
+  if (lane == 63) wtot[wave] = x;
   __syncthreads();
+  int before = 0, NB = 0;
+#pragma unroll
+  for (int w = 0; w < C::WAVES; ++w) {
+    before += w < wave ? wtot[w] : 0;
+    NB += wtot[w];
+  }
+  {
+    int run = before + x - local;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      run += nbv[i];
+      if (s_beg + i < ns) pref[s_beg + i] = run;
+    }
+  }
+  __syncthreads();  // the last barrier: from here on every wave runs alone
 
-  // O^T = V^T P^T: 32 tokens (two blocks) per k-step, 16 d per MFMA.
+  // ---- 2. this wave's range
+  const int n_eff = a.Hkv * a.n_hgroups;
+  const int gid = blockIdx.x * C::WAVES + wave;
+  const int geff = gid % n_eff, w = gid / n_eff;
+  if (w >= a.streams) return;
+  const long long nstreams = a.streams;
+  const int r_beg = (int)((long long)w * NB / nstreams);
+  const int r_end = (int)((long long)(w + 1) * NB / nstreams);
+  if (r_beg >= r_end) return;
+  const int g = geff / a.n_hgroups, hg = geff % a.n_hgroups;
+  const int hj = hg * 16 + c16;  // this lane's query head inside the KV head's group
+  const bool head_ok = hj < a.group;
+  const int hq = g * a.group + (head_ok ? hj : 0);
+
+  // Per-lane offsets.  Direct-to-LDS load j of a tile: lane -> row
+  // LPI*j + lane/CPR, physical chunk lane%CPR holding logical chunk
+  // (lane%CPR) ^ swizzle(row).
+  const uint32_t tok_stride = (uint32_t)a.Hkv * C::ROW;  // bytes between tokens
+  uint32_t kdo[C::IPT], vdo[C::IPT];
+#pragma unroll
+  for (int j = 0; j < C::IPT; ++j) {
+    const int t = C::LPI * j + lane / C::CPR, pc = lane % C::CPR;
+    kdo[j] = t * tok_stride + ((pc ^ dk_swz<D>(t)) << 4);
+    vdo[j] = t * tok_stride + ((pc ^ dv_swz<D>(t)) << 4);
+  }
+  // K operand of k-step ks: row c16, logical chunk KS*G + ks (the lane group G
+  // owns head-dim elements [D/4*G, D/4*(G+1)); Q uses the same order).
+  int koff[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) koff[ks] = c16 * D + (((C::KS * G + ks) ^ dk_swz<D>(c16)) << 3);
+  // V^T operand of d-block db: rows 4G + c16/4, columns 16*db + 4*(c16%4)..+3.
+  int voff[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) {
+    const int r = 4 * G + (c16 >> 2), col = 16 * db + 4 * (c16 & 3);
+    voff[db] = r * D + ((((col >> 3) ^ dv_swz<D>(r)) << 3) + 4 * ((col >> 2) & 1));
+  }
+  // Query operand of k-step ks: head hj, head-dim chunk KS*G + ks (byte
+  // offset inside the KV head's group of query rows).
+  const uint32_t qoff = (uint32_t)((head_ok ? hj : 0) * C::ROW + ((D / 4) * G) * 2);
+  const E* kbase = (const E*)a.k_cache + (size_t)g * D;
+  const E* vbase = (const E*)a.v_cache + (size_t)g * D;
+  const size_t blk_elems = (size_t)C::BS * a.Hkv * D;
+  const float sl2 = a.scale_log2;
+
   f32x4 oacc[C::DB];
 #pragma unroll
-  for (int d = 0; d < C::DB; ++d) oacc[d] = f32x4{};
+  for (int db = 0; db < C::DB; ++db) oacc[db] = f32x4{};
+  float m_ref = -INFINITY, l_run = 0.f;
+  u32x4_t qcur[C::KS];
+  // Query operand for sequence s: 16-byte chunks KS*G + ks of head hj.
+  auto load_q_sync = [&](int s) {
+    const rsrc_t rq = make_rsrc((const E*)a.q + ((size_t)s * a.Hq + g * a.group) * D, (uint32_t)(a.group * C::ROW));
+    uint32_t qo[C::KS];
 #pragma unroll
-  for (int ks = 0; ks < C::BPW / 2; ++ks) {
-    const int r0 = (2 * ks) * C::BS + 4 * g4 + (l16 >> 2);
-    const int r1 = r0 + C::BS;
-#pragma unroll
-    for (int d = 0; d < C::DB; ++d) {
-      const int col = 16 * d + 4 * (l16 & 3);
-      const int ch = col >> 3, hf = (col >> 2) & 1;
-      const E* p0 = wv + r0 * D + (((ch ^ dv_swz<D>(r0)) << 3) + 4 * hf);
-      const E* p1 = wv + r1 * D + (((ch ^ dv_swz<D>(r1)) << 3) + 4 * hf);
-      const V8 vf = cat4<V4, V8>(TT::read_tr(p0), TT::read_tr(p1));
-      oacc[d] = TT::mfma16(vf, pf[ks], oacc[d]);
+    for (int ks = 0; ks < C::KS; ++ks) qo[ks] = qoff + 16 * ks;
+    if constexpr (C::KS == 4) buf_load16_x4_sync(qcur, rq, qo);
+    else buf_load16_x2_sync(qcur, rq, qo);
+  };
+
+  // Windows of up to 64 units: lane i describes unit i.  The loads of the
+  // unit DEPTH-1 ahead are issued before each unit is computed; a unit's LDS
+  // reads wait until only the loads of the units issued after it (up to
+  // DEPTH-1 of them, OPS each) remain outstanding.  Stores issued in between
+  // only make that wait longer, never too short.
+  for (int wb = r_beg; wb < r_end; wb += 64) {
+    const int n = min(64, r_end - wb);
+    int u_pb = 0, u_ntok = 0, u_s = 0, u_fl = 0;
+    if (lane < n) {
+      const int B = wb + lane;
+      int lo = 0, hi = ns - 1;  // first sequence whose inclusive prefix exceeds B
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (pref[mid] > B) hi = mid;
+        else lo = mid + 1;
+      }
+      const int s = lo;
+      const int incl = pref[s], excl = s ? pref[s - 1] : 0;
+      const int b = B - excl;
+      const int ctx = min(max(a.ctx_lens[s], 0), cap);
+      const int pb = a.block_table[(size_t)s * a.max_blocks_per_seq + b];
+      u_pb = min(max(pb, 0), a.num_blocks - 1);
+      u_ntok = min(C::BS, ctx - C::BS * b);
+      u_s = s;
+      const int first = (B == r_beg) || (B == excl);   // the range's first unit of this sequence
+      const int last = (B + 1 == r_end) || (B + 1 == incl);
+      const int whole = (r_beg <= excl) && (r_end >= incl);
+      u_fl = first | (last << 1) | (whole << 2);
     }
-  }
+    // The window's first sequence: its query rows, before any tile load.
+    load_q_sync(__builtin_amdgcn_readlane(u_s, 0));
 
-  // Merge the 4 wave partials of this chunk.
-  if (g4 == 0) {
-    sm_m[wave][l16] = mx;
-    sm_l[wave][l16] = lsum;
-  }
-  __syncthreads();  // also: every wave is done reading its V from LDS
-  float M = -INFINITY;
+    // K and V tiles of unit u into pipeline slot J.
+    auto issue = [&](int u, auto slot) {
+      constexpr int J = decltype(slot)::value;
+      E* kd = (J == 0 ? kb0 : J == 1 ? kb1 : J == 2 ? kb2 : kb3) + wave * C::TILE;
+      E* vd = (J == 0 ? vb0 : J == 1 ? vb1 : J == 2 ? vb2 : vb3) + wave * C::TILE;
+      const int pb = __builtin_amdgcn_readlane(u_pb, u);
+      const int ntok = __builtin_amdgcn_readlane(u_ntok, u);
+      const uint32_t range = (uint32_t)(ntok - 1) * tok_stride + C::ROW;
+      const rsrc_t rk = make_rsrc(kbase + (size_t)pb * blk_elems, range);
+      const rsrc_t rv = make_rsrc(vbase + (size_t)pb * blk_elems, range);
 #pragma unroll
-  for (int w = 0; w < C::WAVES; ++w) M = fmaxf(M, sm_m[w][l16]);
-  const float mb = (M == -INFINITY) ? 0.f : M;
-  const float wscale = fast_exp2(mx - mb);
+      for (int j = 0; j < C::IPT; ++j) buf_load16_lds(rk, kdo[j], kd + j * 512);
+#pragma unroll
+      for (int j = 0; j < C::IPT; ++j) buf_load16_lds(rv, vdo[j], vd + j * 512);
+    };
 
-  float* so = (float*)sv;  // [wave][head 16][D] fp32, reuses the V area
+    auto compute = [&](int u, auto slot) {
+      constexpr int J = decltype(slot)::value;
+      const uint32_t kt = lds_addr((J == 0 ? kb0 : J == 1 ? kb1 : J == 2 ? kb2 : kb3) + wave * C::TILE);
+      const uint32_t vt = lds_addr((J == 0 ? vb0 : J == 1 ? vb1 : J == 2 ? vb2 : vb3) + wave * C::TILE);
+      const int ntok = __builtin_amdgcn_readlane(u_ntok, u);
+      const int fl = __builtin_amdgcn_readlane(u_fl, u);
+      const int s = __builtin_amdgcn_readlane(u_s, u);
+      // A sequence starting inside the window: reload the query rows (this
+      // waits for every load in flight; it happens once per sequence start).
+      if ((fl & 1) && u > 0) load_q_sync(s);
+      const int after = min(n - 1 - u, C::DEPTH - 1);  // units issued after this one
+      if (after >= 3) wait_vm<3 * C::OPS>();
+      else if (after == 2) wait_vm<2 * C::OPS>();
+      else if (after == 1) wait_vm<C::OPS>();
+      else wait_vm<0>();
+      u32x4_t kf[C::KS];
+      {
+        uint32_t ka[C::KS];
 #pragma unroll
-  for (int d = 0; d < C::DB; ++d)
-    *(f32x4*)(so + (wave * 16 + l16) * D + 16 * d + 4 * g4) = oacc[d] * wscale;
-  __syncthreads();
+        for (int ks = 0; ks < C::KS; ++ks) ka[ks] = kt + 2 * koff[ks];
+        if constexpr (C::KS == 4) lds_read16_x4(kf, ka);
+        else lds_read16_x2(kf, ka);
+      }
+      // S^T = K Q^T: register r of lane = (token 4G + r, head c16)
+      f32x4 sacc = f32x4{};
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
+        sacc = TT::mfma16(__builtin_bit_cast(V8, kf[ks]), __builtin_bit_cast(V8, qcur[ks]), sacc);
+      float xs[4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        xs[r] = (4 * G + r < ntok) ? sacc[r] * sl2 : -INFINITY;
+        mx = fmaxf(mx, xs[r]);
+      }
+      mx = max_xor16(mx);
+      mx = max_xor32(mx);  // finite: every unit holds at least one token
+      const bool need = mx > m_ref + kDecRescaleThreshold;
+      if (__any(need)) {
+        const float alpha = need ? fast_exp2(m_ref - mx) : 1.f;
+        m_ref = need ? mx : m_ref;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) oacc[db] *= alpha;
+      }
+      V4 pf;
+      float ps = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = fast_exp2(xs[r] - m_ref);
+        ps += p;
+        pf[r] = TT::cvt(p);
+      }
+      l_run += ps;
+      // O^T += V^T P^T: P^T's operand is exactly the S^T register layout.
+      u32x2_t vf[C::DB];
+      {
+        uint32_t va[C::DB];
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) va[db] = vt + 2 * voff[db];
+        if constexpr (C::DB == 8) lds_read_tr8_x8(vf, va);
+        else lds_read_tr8_x4(vf, va);
+      }
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) oacc[db] = TT::mfma16k16(__builtin_bit_cast(V4, vf[db]), pf, oacc[db]);
 
-  // 16 heads x D outputs, D/16 per thread; thread -> (head, 16 consecutive d / (128/D)).
-  constexpr int PER = 16 * D / C::NT;
-  const int oh = tid / (D / PER), od = (tid % (D / PER)) * PER;
-  const int ohj = hg * 16 + oh;
-  if (ohj < a.group) {
-    const int ohq = g * a.group + ohj;
-    float Lh = 0.f, Mh = -INFINITY;
+      // End of a sequence's run inside this range: write the output (the
+      // range holds the whole sequence) or a partial, and restart the state.
+      if (fl & 2) {
+        float lt = sum_xor16(l_run);
+        lt = sum_xor32(lt);
+        const float inv = 1.f / lt;
+        const float lse2 = m_ref + log2f(lt);
+        if (head_ok) {
+          if (fl & 4) {
+            E* orow = (E*)a.o + ((size_t)s * a.Hq + hq) * D + 4 * G;
 #pragma unroll
-    for (int w = 0; w < C::WAVES; ++w) Mh = fmaxf(Mh, sm_m[w][oh]);
-    const float mbh = (Mh == -INFINITY) ? 0.f : Mh;
+            for (int db = 0; db < C::DB; ++db) {
+              V4 o4;
 #pragma unroll
-    for (int w = 0; w < C::WAVES; ++w) Lh += sm_l[w][oh] * fast_exp2(sm_m[w][oh] - mbh);
-    const float inv = Lh > 0.f ? 1.f / Lh : 0.f;
-    const size_t pidx = ((size_t)s * a.Hq + ohq) * a.n_split + c;
-    float* dst = a.ws_o + pidx * D + od;
+              for (int r = 0; r < 4; ++r) o4[r] = TT::cvt(oacc[db][r] * inv);
+              *(V4*)(orow + 16 * db) = o4;
+            }
+            if (G == 0 && a.lse != nullptr) a.lse[(size_t)s * a.Hq + hq] = lse2 * kLn2;
+          } else {
+            const size_t slot_id = (size_t)w + s;
+            float* dst = a.ws_o + (slot_id * a.Hq + hq) * D + 4 * G;
 #pragma unroll
-    for (int e = 0; e < PER; e += 4) {
-      f32x4 acc = f32x4{};
+            for (int db = 0; db < C::DB; ++db) *(f32x4*)(dst + 16 * db) = oacc[db] * inv;
+            if (G == 0) a.ws_lse[slot_id * a.Hq + hq] = lse2;
+          }
+        }
+        m_ref = -INFINITY;
+        l_run = 0.f;
 #pragma unroll
-      for (int w = 0; w < C::WAVES; ++w) acc += *(const f32x4*)(so + (w * 16 + oh) * D + od + e);
-      *(f32x4*)(dst + e) = acc * inv;
+        for (int db = 0; db < C::DB; ++db) oacc[db] = f32x4{};
+      }
+    };
+
+    auto step = [&](int u, auto slot) {
+      constexpr int J = decltype(slot)::value;
+      if (u < n) {
+        if (u + C::DEPTH - 1 < n) issue(u + C::DEPTH - 1, Slot<(J + C::DEPTH - 1) % C::DEPTH>{});
+        compute(u, slot);
+      }
+    };
+
+    issue(0, Slot<0>{});
+    if (1 < n) issue(1, Slot<1>{});
+    if (2 < n) issue(2, Slot<2>{});
+    for (int u0 = 0; u0 < n; u0 += C::DEPTH) {
+      step(u0, Slot<0>{});
+      step(u0 + 1, Slot<1>{});
+      step(u0 + 2, Slot<2>{});
+      step(u0 + 3, Slot<3>{});
     }
-    if (od == 0) a.ws_lse[pidx] = Lh > 0.f ? mbh + log2f(Lh) : -INFINITY;
   }
 }
 
+// Merge of split sequences: one wave per (sequence, HPW query heads), each
+// lane owning 4 consecutive outputs of one head.  The wave loads the partials
+// of up to 16 ranges at once, so a sequence spread over <= 16 ranges costs one
+// round trip to memory after the block counts.
 template <typename TT, int D>
-__global__ __launch_bounds__(D) void decode_combine_kernel(DecArgs a) {
+__global__ __launch_bounds__(64) void decode_combine_kernel(DecArgs a) {
   using E = typename TT::elem;
-  const int s = blockIdx.x / a.Hq, hq = blockIdx.x % a.Hq;
-  const int d = threadIdx.x;
-  const int ctx = min(max(a.ctx_lens[s], 0), a.max_blocks_per_seq * 16);
-  const int nc = (ctx + kDecodeChunk - 1) / kDecodeChunk;
-  const size_t pbase = ((size_t)s * a.Hq + hq) * a.n_split;
-  float M = -INFINITY;
-  for (int c = 0; c < nc; ++c) M = fmaxf(M, a.ws_lse[pbase + c]);
-  const float mb = (M == -INFINITY) ? 0.f : M;
-  float acc = 0.f, wsum = 0.f;
-  for (int c = 0; c < nc; ++c) {
-    const float w = fast_exp2(a.ws_lse[pbase + c] - mb);
-    wsum += w;
-    acc += w * a.ws_o[(pbase + c) * D + d];
+  using V4 = typename TT::vec4;
+  constexpr int D4 = D / 4, HPW = 64 / D4;
+  const int n_hb = (a.Hq + HPW - 1) / HPW;
+  const int s = blockIdx.x / n_hb, hb = blockIdx.x % n_hb;
+  const int lane = threadIdx.x;
+  const int hq = hb * HPW + lane / D4, d4 = lane % D4;
+  const bool lane_ok = hq < a.Hq;
+  const int cap = a.max_blocks_per_seq * 16;
+
+  // NB (all sequences) and the blocks before sequence s, as the split kernel
+  // counted them.
+  int tot = 0, bef = 0;
+  for (int j0 = 0; j0 < a.num_seqs; j0 += 8 * 64) {
+    int c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int j = j0 + 64 * i + lane;
+      c[i] = j < a.num_seqs ? a.ctx_lens[j] : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int j = j0 + 64 * i + lane;
+      const int nb = (min(max(c[i], 0), cap) + 15) >> 4;
+      tot += nb;
+      bef += j < s ? nb : 0;
+    }
   }
-  const float o = wsum > 0.f ? acc / wsum : 0.f;
-  ((E*)a.o)[((size_t)s * a.Hq + hq) * D + d] = TT::cvt(o);
-  if (a.lse != nullptr && d == 0)
-    a.lse[(size_t)s * a.Hq + hq] = wsum > 0.f ? (mb + log2f(wsum)) * kLn2 : -INFINITY;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    tot += __shfl_xor(tot, off);
+    bef += __shfl_xor(bef, off);
+  }
+  const int NB = tot, S0 = bef;
+  const int nb_s = (min(max(a.ctx_lens[s], 0), cap) + 15) >> 4;
+  E* orow = (E*)a.o + ((size_t)s * a.Hq + hq) * D + 4 * d4;
+  if (nb_s == 0) {  // no context: out = 0, lse = -inf
+    if (lane_ok) {
+      *(V4*)orow = V4{};
+      if (d4 == 0 && a.lse != nullptr) a.lse[(size_t)s * a.Hq + hq] = -INFINITY;
+    }
+    return;
+  }
+  const long long W = a.streams;
+  // Range holding global block X: the largest w with floor(w*NB/W) <= X.
+  const int w_lo = (int)(((long long)(S0 + 1) * W + NB - 1) / NB) - 1;
+  const int w_hi = (int)(((long long)(S0 + nb_s) * W + NB - 1) / NB) - 1;
+  if (w_lo == w_hi || !lane_ok) return;  // one range held the whole sequence and wrote it
+
+  // With NB >= W every range holds a block.  Otherwise (NB * W < W^2 fits
+  // 32 bits) a range w holds one iff floor(w*NB/W) < floor((w+1)*NB/W).
+  const bool all_live = NB >= a.streams;
+  const unsigned nb32 = (unsigned)NB, w32 = (unsigned)a.streams;
+  float M = -INFINITY, wsum = 0.f;
+  f32x4 acc = f32x4{};
+  for (int base = w_lo; base <= w_hi; base += 16) {
+    float L[16];
+    f32x4 O[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int w = base + k;
+      // a range that holds no block left no partial
+      const bool ok = w <= w_hi && (all_live || ((unsigned)w * nb32) / w32 < ((unsigned)(w + 1) * nb32) / w32);
+      const size_t slot = (size_t)w + s;
+      L[k] = ok ? a.ws_lse[slot * a.Hq + hq] : -INFINITY;
+      O[k] = ok ? *(const f32x4*)(a.ws_o + (slot * a.Hq + hq) * D + 4 * d4) : f32x4{};
+    }
+    float mloc = M;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) mloc = fmaxf(mloc, L[k]);
+    const float sc = M == -INFINITY ? 0.f : fast_exp2(M - mloc);
+    wsum *= sc;
+    acc *= sc;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float wt = L[k] == -INFINITY ? 0.f : fast_exp2(L[k] - mloc);
+      wsum += wt;
+      acc += wt * O[k];
+    }
+    M = mloc;
+  }
+  const float inv = 1.f / wsum;
+  V4 o4;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) o4[r] = TT::cvt(acc[r] * inv);
+  *(V4*)orow = o4;
+  if (d4 == 0 && a.lse != nullptr) a.lse[(size_t)s * a.Hq + hq] = (M + log2f(wsum)) * kLn2;
 }
 
 template <typename TT, int D>
 static hipError_t launch_decode_t(const DecArgs& a, hipStream_t stream) {
-  const long long blocks = (long long)a.num_seqs * a.Hkv * a.n_hgroups * a.n_split;
+  const long long waves = (long long)a.streams * a.Hkv * a.n_hgroups;
+  const long long blocks = (waves + DecCfg<D>::WAVES - 1) / DecCfg<D>::WAVES;
   hipLaunchKernelGGL((decode_split_kernel<TT, D>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<TT, D>), dim3((unsigned)(a.num_seqs * a.Hq)), dim3(D), 0, stream, a);
+  constexpr int HPW = 64 / (D / 4);
+  const long long cblocks = (long long)a.num_seqs * ((a.Hq + HPW - 1) / HPW);
+  hipLaunchKernelGGL((decode_combine_kernel<TT, D>), dim3((unsigned)cblocks), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -21,6 +21,13 @@ struct FwdArgs {
   int n_qblocks;
 };
 
+// Paged decode.  The cache blocks of all sequences, taken in sequence order,
+// form one list of NB = sum_s ceil(ctx_s / 16) blocks; it is cut into
+// `streams` equal contiguous ranges per (KV head, query-head group), and each
+// range is one wave's work.  A wave whose range holds a whole sequence writes
+// that sequence's output directly; otherwise it leaves a partial (normalised
+// output, log2-sum-exp) in the workspace slot (range index + sequence index),
+// and the combine kernel merges the partials of each sequence.
 struct DecArgs {
   const void* q;
   const void* k_cache;
@@ -28,19 +35,23 @@ struct DecArgs {
   const int32_t* block_table;
   const int32_t* ctx_lens;
   void* o;
-  float* lse;  // may be null
-  float* ws_o;    // [num_seqs, Hq, n_split, D] partial outputs (normalised)
-  float* ws_lse;  // [num_seqs, Hq, n_split] partial log2-sum-exp
+  float* lse;     // may be null
+  float* ws_o;    // [slots, Hq, D] partial outputs (normalised)
+  float* ws_lse;  // [slots, Hq] partial log2-sum-exp
   int num_seqs, Hq, Hkv, group, max_blocks_per_seq, num_blocks;
-  int n_split;     // context chunks per sequence
-  int n_hgroups;   // ceil(group / 16): query-head groups of one KV head
+  int n_hgroups;  // ceil(group / 16): query-head groups of one KV head
+  int streams;    // ranges per (KV head, head group)
   float scale_log2;
 };
 
-// Tokens handled by one decode work-group (4 waves x 4 blocks x 16 tokens).
-constexpr int kDecodeChunk = 256;
 constexpr int kPrefillBlockM = 128;
 constexpr float kLog2e = 1.44269504088896340736f;
+
+// Decode launch limits.  Larger batches are cut into several launches.
+constexpr int kDecodeMaxSeqsPerLaunch = 2048;
+constexpr int kDecodeMaxStreams = 2048;
+// Waves of the split kernel resident on one CU (one 4-wave work-group).
+constexpr int kDecodeWavesPerCU = 4;
 
 hipError_t launch_fwd(const FwdArgs& a, int D, int dtype, hipStream_t stream);
 hipError_t launch_decode(const DecArgs& a, int D, int dtype, hipStream_t stream);
