@@ -18,9 +18,11 @@
 //   buffered; global loads for tile t+1 are in flight while tile t computes)
 //   and shared by the 4 waves.  Causal and sliding-window masks are applied
 //   as a key-tile range [t_lo, t_hi) per work-group, so fully masked tiles are
-//   never loaded; a wave skips tiles that its own rows cannot see, and only
-//   tiles that straddle a mask edge (or the end of the keys) pay for an
-//   element-wise mask.  Causal work-groups are issued heaviest first.
+//   never loaded, and only tiles that straddle a mask edge (or the end of the
+//   keys) pay for an element-wise mask.  Work-group ids go round-robin over
+//   the 8 XCDs; when the KV groups divide evenly, each XCD takes whole KV
+//   groups (the query heads sharing one K/V stay in one L2) and issues its
+//   q-blocks heaviest first (causal).
 //
 // Per 64-key tile and wave (all MFMA 32x32x16, fp32 accumulate):
 //   S^T = K Q^T  : A = K rows from LDS, B = the wave's Q rows (registers).
@@ -30,10 +32,17 @@
 //   O^T += V^T P^T: A = V^T fetched from the natural [key][d] LDS tile with
 //                  the LDS transpose read, B = P straight from the S^T
 //                  accumulators (rounded to the input type), no shuffles.
+// The loop is software-pipelined: while tile t's exponentials run on the
+// vector ALU, the MFMA unit works on tile t's P.V (16 keys at a time, each
+// step right after its probabilities) and on tile t+1's scores, so the two
+// units overlap inside one wave.
 //
 // LDS: 2 stages x (K tile + V tile) x 64 x D x 2 B = 64 KiB at D = 128, so two
 // work-groups fit in the 160 KiB of a CU.  16-byte chunks of each row are
-// XOR-swizzled by row so the MFMA operand reads hit distinct banks.
+// XOR-swizzled by row so the MFMA operand reads hit distinct banks.  Each of
+// the four tile buffers is an LDS array of its own and the loop is unrolled
+// by two, so every read names its buffer and the compiler waits only for the
+// global->LDS loads that fill it, never for the ones landing in the others.
 #include "common.h"
 #include "internal.h"
 
@@ -91,16 +100,21 @@ __device__ __forceinline__ uint32_t pack2<F16>(float a, float b) {
   return __builtin_bit_cast(uint32_t, (v2){(_Float16)a, (_Float16)b});
 }
 
+template <int P>
+struct Par {
+  static constexpr int value = P;
+};
+
 template <typename TT, int D>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   using C = FwdCfg<D>;
   using E = typename TT::elem;
   using V8 = typename TT::vec8;
   using V4 = typename TT::vec4;
-  // [K tile 0][K tile 1][V tile 0][V tile 1]; K runs one tile ahead of V.
-  __shared__ __attribute__((aligned(16))) E smem[4 * C::TILE];
-  E* const kbuf = smem;
-  E* const vbuf = smem + 2 * C::TILE;
+  __shared__ __attribute__((aligned(16))) E kt0[C::TILE];
+  __shared__ __attribute__((aligned(16))) E kt1[C::TILE];
+  __shared__ __attribute__((aligned(16))) E vt0[C::TILE];
+  __shared__ __attribute__((aligned(16))) E vt1[C::TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -109,12 +123,29 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   const int j16 = lane & 15, grp = lane >> 4;
 
   // ---- which (q-block, head, batch)
-  const int per_qb = a.Hq * a.B;
-  const int qb_rank = blockIdx.x / per_qb;
-  const int rem = blockIdx.x - qb_rank * per_qb;
-  const int hq = rem % a.Hq, b = rem / a.Hq;
+  int qb_rank, gid, hj;
+  {
+    const int n_groups = a.B * a.Hkv;
+    if ((n_groups & 7) == 0) {
+      // XCD x (= blockIdx mod 8) takes the KV groups x, x+8, ...; its
+      // work-groups walk q-block ranks, heaviest first when causal.
+      const int x = blockIdx.x & 7, k = blockIdx.x >> 3;
+      const int row = (n_groups >> 3) * a.group;  // work-groups per q-block rank on one XCD
+      qb_rank = k / row;
+      const int r = k - qb_rank * row;
+      gid = x + 8 * (r / a.group);
+      hj = r % a.group;
+    } else {
+      const int row = n_groups * a.group;
+      qb_rank = blockIdx.x / row;
+      const int r = blockIdx.x - qb_rank * row;
+      gid = r / a.group;
+      hj = r % a.group;
+    }
+  }
+  const int b = gid / a.Hkv, g = gid % a.Hkv;
+  const int hq = g * a.group + hj;
   const int qb = a.causal ? (a.n_qblocks - 1 - qb_rank) : qb_rank;
-  const int g = hq / a.group;
   const int q0 = qb * C::BM;
   const int off = a.Lk - a.Lq;  // bottom-right alignment of the causal diagonal
   const int W = a.window;
@@ -162,9 +193,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   }
   const int wr_lo = q0 + wave * 32;
   const int wr_hi = min(wr_lo + 31, a.Lq - 1);
-  const bool wave_live = wr_lo < a.Lq;
 
-  // ---- per-lane LDS element offsets inside a tile (hoisted out of the loop)
+  // ---- per-lane LDS element offsets inside a tile
   int koff[C::KSTEPS];  // K operand of k-step s, first 32-key half (+32*D for the second)
 #pragma unroll
   for (int s = 0; s < C::KSTEPS; ++s) koff[s] = l32 * D + (((2 * s + hh) ^ k_swz<D>(l32)) << 3);
@@ -220,18 +250,30 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     return (jt + C::BN <= a.Lk) && (!a.causal || jt + C::BN - 1 <= wr_lo + off) &&
            (W < 0 || jt >= wr_hi + off - W) && (W < 0 || a.causal || jt + C::BN - 1 <= wr_lo + off + W);
   };
-  // S^T = K Q^T for one tile: two 32-key halves of raw fp32 scores.
-  auto qk = [&](const E* kt, f32x16* sacc) {
-    sacc[0] = f32x16{};
-    sacc[1] = f32x16{};
+  // Element-wise mask of tile t's scores: key (kh*32 + 8*(r/4) + 4*hh + r%4)
+  // of the tile is visible to row qi iff it lies in [jlo_row, jhi_row].
+  auto mask_tile = [&](int t, f32x16* s) {
+    const int base = t * C::BN + 4 * hh;
+    const int lo = jlo_row - base, hi = jhi_row - base;
+    const uint32_t span = (uint32_t)(hi - lo);
 #pragma unroll
-    for (int s = 0; s < C::KSTEPS; ++s) {
+    for (int kh = 0; kh < 2; ++kh) {
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-        const V8 kf = *(const V8*)(kt + koff[s] + kh * 32 * D);
-        sacc[kh] = TT::mfma32(kf, qf[s], sacc[kh]);
+      for (int r = 0; r < 16; ++r) {
+        const int rel = kh * 32 + 8 * (r >> 2) + (r & 3);
+        const bool ok = hi >= lo && (uint32_t)(rel - lo) <= span;
+        s[kh][r] = ok ? s[kh][r] : -INFINITY;
       }
     }
+  };
+  // Row maximum of raw scores (lane and lane^32 share a row).
+  auto row_max = [&](const f32x16* s) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kh][r]);
+    return max_xor32(mx);
   };
 
   f32x16 oacc[C::DB];
@@ -239,84 +281,26 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   for (int d = 0; d < C::DB; ++d) oacc[d] = f32x16{};
   float m_ref = -INFINITY;  // exponent base of this row (base-2 units)
   float l_run = 0.f;        // this lane's share of the row sum
+  f32x16 scur[2];           // raw scores of the current tile, masked
+  float mx_cur = -INFINITY; // their row maximum
 
-  // P = 2^(s*scale*log2e - base) for the tile in `sc`, its row sums, and
-  // O^T += V^T P^T, 16 keys per MFMA k-step.  Key order inside a step is the
-  // one the S^T accumulator hands out: operand index 8*hh + e is key
-  // 16*s + 8*(e/4) + 4*hh + e%4.  The two transposed reads fetch exactly
+  // One tile: K(t+2) and V(t+1) start loading into the buffers K(t) and
+  // V(t-1) left; tile t's statistics update; then, per 16-key step s, the
+  // step's probabilities (exp2 of one FMA on the raw scores), its P.V MFMAs,
+  // and a quarter of tile t+1's S^T = K Q^T.  The key order inside a step is
+  // the one the S^T accumulator hands out: operand index 8*hh + e is key
+  // 16*s + 8*(e/4) + 4*hh + e%4, and the two transposed reads fetch exactly
   // those V rows for column d = 32*db + 16*(group&1) + (lane&15).
-  auto softmax_pv = [&](const f32x16* sc, const E* vt, float nb) {
-    uint32_t pw[4][4];
-    float rs = 0.f;
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = fast_exp2(__builtin_fmaf(sc[kh][r], sl2, nb));
-        const float p1 = fast_exp2(__builtin_fmaf(sc[kh][r + 1], sl2, nb));
-        rs += p0 + p1;
-        pw[2 * kh + (r >> 3)][(r & 7) >> 1] = pack2<TT>(p0, p1);
-      }
-    }
-    l_run += rs;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const V8 pf = __builtin_bit_cast(V8, make_uint4(pw[s][0], pw[s][1], pw[s][2], pw[s][3]));
-#pragma unroll
-      for (int d = 0; d < C::DB; ++d) {
-        const E* p0 = vt + voff[d] + 16 * s * D;
-        const V8 vf = cat4<V4, V8>(TT::read_tr(p0), TT::read_tr(p0 + 8 * D));
-        oacc[d] = TT::mfma32(vf, pf, oacc[d]);
-      }
-    }
-  };
+  auto body = [&](int t, auto par) {
+    constexpr int P = decltype(par)::value;
+    const E* kn = P ? kt0 : kt1;  // K(t+1)
+    const E* vc = P ? vt1 : vt0;  // V(t)
+    load_k(t + 2, P ? kt1 : kt0);
+    load_v(t + 1, P ? vt0 : vt1);
 
-  f32x16 scur[2];
-  if (t_lo < t_hi) {
-    load_k(t_lo, kbuf);
-    load_v(t_lo, vbuf);
-    load_k(t_lo + 1, kbuf + C::TILE);
-    wait_vmem();
-    __syncthreads();
-    qk(kbuf, scur);
-    __syncthreads();  // K(t_lo)'s buffer is refilled by the first iteration
-  }
-
-  for (int t = t_lo; t < t_hi; ++t) {
-    const int i = t - t_lo;
-    // Loads for the next iteration: K(t+2) into the buffer K(t) used, V(t+1)
-    // into the buffer V(t-1) used.  They land while this tile computes.
-    load_k(t + 2, kbuf + (i & 1) * C::TILE);
-    load_v(t + 1, vbuf + ((i + 1) & 1) * C::TILE);
-
-    if (!tile_full(t)) {  // element-wise mask, only on edge tiles
-      // Keys row qi may see, relative to this lane's first key of the tile:
-      // key (kh*32 + 8*(r/4) + r%4) is visible iff it lies in [lo, hi].
-      const int base = t * C::BN + 4 * hh;
-      const int lo = jlo_row - base, hi = jhi_row - base;
-      const uint32_t span = (uint32_t)(hi - lo);
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int rel = kh * 32 + 8 * (r >> 2) + (r & 3);
-          const bool ok = hi >= lo && (uint32_t)(rel - lo) <= span;
-          scur[kh][r] = ok ? scur[kh][r] : -INFINITY;
-        }
-      }
-    }
-
-    // Row maximum of the raw scores (lane and lane^32 share a row).
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, scur[kh][r]);
-    mx = max_xor32(mx);
-    const float m_new = mx * sl2;  // sl2 > 0 keeps the order; -inf stays -inf
-
-    // Move the exponent base only when the maximum has grown by more than the
-    // threshold somewhere in the wave; rescale those rows.
+    // Move the exponent base only when the maximum has grown by more than
+    // the threshold somewhere in the wave; rescale those rows.
+    const float m_new = mx_cur * sl2;  // sl2 > 0 keeps the order; -inf stays -inf
     const bool need = m_new > m_ref + kRescaleThreshold;
     if (__any(need)) {
       if (need) {
@@ -328,62 +312,128 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       }
     }
     const float nb = (m_ref == -INFINITY) ? 0.f : -m_ref;
-    const E* vt = vbuf + (i & 1) * C::TILE;
 
-    {
-      // One straight-line block that software-pipelines the next tile's
-      // S^T = K Q^T with this tile's softmax: per k-step, the K operands of
-      // the following step are read, the two MFMAs of this step issue, and a
-      // share of this tile's exponentials, row sums and P packing runs on the
-      // vector ALU while those MFMAs execute.  Then O^T += V^T P^T.  On the
-      // last tile the next-tile product reads a stale buffer and is discarded
-      // (cheaper than a second copy of the block).  sched_barrier keeps the
-      // compiler from regrouping the steps.
-      constexpr int EPS = 32 / C::KSTEPS;  // score elements exponentiated per k-step
-      const E* kt = kbuf + ((i + 1) & 1) * C::TILE;
-      f32x16 snext[2] = {f32x16{}, f32x16{}};
-      uint32_t pw[4][4];
-      float rs = 0.f;
-      V8 kcur0 = *(const V8*)(kt + koff[0]);
-      V8 kcur1 = *(const V8*)(kt + koff[0] + 32 * D);
+    // The tile as 8 groups of G MFMAs (G = D/32), in the order
+    //   Q0 Q1 P0 Q2 P1 Q3 P2 P3
+    // Qk = 1/4 of the next tile's S^T (Q0-Q1 build keys 0-31, Q2-Q3 keys
+    // 32-63, so the second half takes over the registers of this tile's first
+    // half); Ps = P.V of key step s (16 keys).  A wave issues in order and an
+    // MFMA waits for the matrix unit, so the vector-ALU work has to sit
+    // between MFMAs, in small even portions: this tile's 32 probabilities
+    // (one FMA, one exp2 and one add each; pairs are packed to the input type)
+    // are spread over the first 7G MFMAs so that each step's are done before
+    // its P.V group, and the next tile's row maximum over the rest.  Each
+    // group's LDS operands are read during the group before it;
+    // sched_barrier keeps every MFMA in its own scheduling region.
+    constexpr int G = C::DB;         // MFMAs per group (KSTEPS/2 == D/32)
+    constexpr int NSLOT = 8 * G;     // MFMAs per tile
+    constexpr int NEXP = 7 * G;      // slots that carry probabilities
+    static_assert(C::KSTEPS / 2 == G, "Q and P groups have the same size");
+    f32x16 snext[2];
+    float rs = 0.f, mnext = -INFINITY;
+    float pv[4][8];
+    uint32_t pw[4][4];
+    V8 kop[4][G], vop[4][G];
+    auto read_k = [&](int q) {
 #pragma unroll
-      for (int s = 0; s < C::KSTEPS; ++s) {
-        V8 knext0 = kcur0, knext1 = kcur1;
-        if (s + 1 < C::KSTEPS) {
-          knext0 = *(const V8*)(kt + koff[s + 1]);
-          knext1 = *(const V8*)(kt + koff[s + 1] + 32 * D);
-        }
-        snext[0] = TT::mfma32(kcur0, qf[s], snext[0]);
-        snext[1] = TT::mfma32(kcur1, qf[s], snext[1]);
+      for (int k = 0; k < G; ++k) kop[q][k] = *(const V8*)(kn + koff[(q & 1) * G + k] + (q >> 1) * 32 * D);
+    };
+    auto read_v = [&](int st) {
 #pragma unroll
-        for (int e = 0; e < EPS; e += 2) {
-          const int f = s * EPS + e;  // flat element index kh*16 + r
-          const int kh = f >> 4, r = f & 15;
-          const float p0 = fast_exp2(__builtin_fmaf(scur[kh][r], sl2, nb));
-          const float p1 = fast_exp2(__builtin_fmaf(scur[kh][r + 1], sl2, nb));
-          rs += p0 + p1;
-          pw[2 * kh + (r >> 3)][(r & 7) >> 1] = pack2<TT>(p0, p1);
-        }
-        kcur0 = knext0;
-        kcur1 = knext1;
-        __builtin_amdgcn_sched_barrier(0);
+      for (int d = 0; d < G; ++d) {
+        const E* p0 = vc + voff[d] + 16 * st * D;
+        vop[st][d] = cat4<V4, V8>(TT::read_tr(p0), TT::read_tr(p0 + 8 * D));
       }
-      l_run += rs;
+    };
+    // Probability of element e (key step e/8, register 8*(step&1) + e%8 of
+    // the S^T half step/2, which holds key 8*(r/4) + 4*hh + r%4 of that half).
+    auto prob = [&](int e) {
+      const int st = e >> 3, j = e & 7, r = 8 * (st & 1) + j;
+      pv[st][j] = fast_exp2(__builtin_fmaf(scur[st >> 1][r], sl2, nb));
+      rs += pv[st][j];
+      if (j & 1) pw[st][j >> 1] = pack2<TT>(pv[st][j - 1], pv[st][j]);
+    };
+    __builtin_amdgcn_sched_barrier(0);
+    read_k(0);
+    read_k(1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const V8 pf = __builtin_bit_cast(V8, make_uint4(pw[s][0], pw[s][1], pw[s][2], pw[s][3]));
-#pragma unroll
-        for (int d = 0; d < C::DB; ++d) {
-          const E* p0 = vt + voff[d] + 16 * s * D;
-          const V8 vf = cat4<V4, V8>(TT::read_tr(p0), TT::read_tr(p0 + 8 * D));
-          oacc[d] = TT::mfma32(vf, pf, oacc[d]);
-        }
+    for (int i = 0; i < NSLOT; ++i) {
+      const int grp_id = i / G, m = i % G;
+      // order Q0 Q1 P0 Q2 P1 Q3 P2 P3: group -> (is_q, index)
+      const int q_of[8] = {0, 1, -1, 2, -1, 3, -1, -1};
+      const int p_of[8] = {-1, -1, 0, -1, 1, -1, 2, 3};
+      if (m == 0) {  // operands of the next group
+        if (grp_id == 0) read_v(0);
+        if (grp_id == 1) read_k(2);
+        if (grp_id == 2) read_v(1);
+        if (grp_id == 3) read_k(3);
+        if (grp_id == 4) read_v(2);
+        if (grp_id == 5) read_v(3);
       }
-      scur[0] = snext[0];
-      scur[1] = snext[1];
+      if (q_of[grp_id] >= 0) {
+        const int q = q_of[grp_id];
+        const f32x16 acc = (m == 0 && (q & 1) == 0) ? f32x16{} : snext[q >> 1];
+        snext[q >> 1] = TT::mfma32(kop[q][m], qf[(q & 1) * G + m], acc);
+      } else {
+        const int st = p_of[grp_id];
+        const V8 pf = __builtin_bit_cast(V8, make_uint4(pw[st][0], pw[st][1], pw[st][2], pw[st][3]));
+        oacc[m] = TT::mfma32(vop[st][m], pf, oacc[m]);
+      }
+      if (i < NEXP) {
+#pragma unroll
+        for (int e = (32 * i) / NEXP; e < (32 * (i + 1)) / NEXP; ++e) prob(e);
+      }
+      // next tile's row maximum: half 0 once Q1 is done, half 1 once Q3 is
+      if (i >= 2 * G && i < 6 * G) {
+#pragma unroll
+        for (int r = (16 * (i - 2 * G)) / (4 * G); r < (16 * (i - 2 * G + 1)) / (4 * G); ++r)
+          mnext = fmaxf(mnext, snext[0][r]);
+      }
+      if (i >= 6 * G) {
+#pragma unroll
+        for (int r = (16 * (i - 6 * G)) / (2 * G); r < (16 * (i - 6 * G + 1)) / (2 * G); ++r)
+          mnext = fmaxf(mnext, snext[1][r]);
+      }
+      if (i == NSLOT - 1) mnext = max_xor32(mnext);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    l_run += rs;
+    mx_cur = mnext;
+    if (!tile_full(t + 1)) {
+      asm volatile("" ::: "memory");  // a real branch: the mask is rare, do not speculate it
+      mask_tile(t + 1, snext);
+      mx_cur = row_max(snext);
+    }
+    scur[0] = snext[0];
+    scur[1] = snext[1];
     wait_vmem();
     __syncthreads();
+  };
+
+  if (t_lo < t_hi) {
+    load_k(t_lo, kt0);
+    load_v(t_lo, vt0);
+    load_k(t_lo + 1, kt1);
+    wait_vmem();
+    __syncthreads();
+    scur[0] = f32x16{};
+    scur[1] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < C::KSTEPS; ++s) {
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        const V8 kf = *(const V8*)(kt0 + koff[s] + kh * 32 * D);
+        scur[kh] = TT::mfma32(kf, qf[s], scur[kh]);
+      }
+    }
+    if (!tile_full(t_lo)) mask_tile(t_lo, scur);
+    mx_cur = row_max(scur);
+    __syncthreads();  // K(t_lo)'s buffer is refilled by the first tile
+  }
+  for (int t = t_lo; t < t_hi; t += 2) {
+    body(t, Par<0>{});
+    if (t + 1 < t_hi) body(t + 1, Par<1>{});
   }
 
   // ---- epilogue: normalise, store O in the input type, and the log-sum-exp
