@@ -18,6 +18,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace attn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -226,5 +229,17 @@ __device__ __forceinline__ float sum_xor16(float x) {
 }
 
 constexpr float kLn2 = 0.69314718055994530942f;
+
+// f(std::integral_constant<int, i>) for i = 0..N-1, expanded at compile time,
+// so that per-iteration indices (register array slots, schedule positions)
+// are constants.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 }  // namespace attn

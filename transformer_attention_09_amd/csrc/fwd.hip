@@ -318,20 +318,22 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     // Qk = 1/4 of the next tile's S^T (Q0-Q1 build keys 0-31, Q2-Q3 keys
     // 32-63, so the second half takes over the registers of this tile's first
     // half); Ps = P.V of key step s (16 keys).  A wave issues in order and an
-    // MFMA waits for the matrix unit, so the vector-ALU work has to sit
-    // between MFMAs, in small even portions: this tile's 32 probabilities
-    // (one FMA, one exp2 and one add each; pairs are packed to the input type)
-    // are spread over the first 7G MFMAs so that each step's are done before
-    // its P.V group, and the next tile's row maximum over the rest.  Each
-    // group's LDS operands are read during the group before it;
-    // sched_barrier keeps every MFMA in its own scheduling region.
+    // MFMA waits for the matrix unit, so the vector-ALU work sits between
+    // MFMAs in small portions, and each piece of it is split over consecutive
+    // MFMAs so that no MFMA waits behind a dependent chain: a probability's
+    // FMA, its exp2 and its sum/pack go after three successive MFMAs.  This
+    // tile's 32 probabilities are spread so that each step's are packed
+    // before its P.V group; the next tile's row maximum (two interleaved
+    // chains) follows its Q groups.  Each group's LDS operands are read two
+    // groups ahead; sched_barrier keeps every MFMA in its own scheduling
+    // region.
     constexpr int G = C::DB;         // MFMAs per group (KSTEPS/2 == D/32)
     constexpr int NSLOT = 8 * G;     // MFMAs per tile
-    constexpr int NEXP = 7 * G;      // slots that carry probabilities
-    static_assert(C::KSTEPS / 2 == G, "Q and P groups have the same size");
+    constexpr int SA = G == 4 ? 26 : 9;  // slots that start a probability
+    static_assert(C::KSTEPS / 2 == G && (G == 4 || G == 2), "Q and P groups have the same size");
     f32x16 snext[2];
-    float rs = 0.f, mnext = -INFINITY;
-    float pv[4][8];
+    float rs = 0.f, mx_a = -INFINITY, mx_b = -INFINITY;
+    float px[32];  // probabilities in flight: exponent argument, then value
     uint32_t pw[4][4];
     V8 kop[4][G], vop[4][G];
     auto read_k = [&](int q) {
@@ -345,59 +347,73 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         vop[st][d] = cat4<V4, V8>(TT::read_tr(p0), TT::read_tr(p0 + 8 * D));
       }
     };
-    // Probability of element e (key step e/8, register 8*(step&1) + e%8 of
-    // the S^T half step/2, which holds key 8*(r/4) + 4*hh + r%4 of that half).
-    auto prob = [&](int e) {
-      const int st = e >> 3, j = e & 7, r = 8 * (st & 1) + j;
-      pv[st][j] = fast_exp2(__builtin_fmaf(scur[st >> 1][r], sl2, nb));
-      rs += pv[st][j];
-      if (j & 1) pw[st][j >> 1] = pack2<TT>(pv[st][j - 1], pv[st][j]);
+    // Element e: key step e/8, register 8*(step&1) + e%8 of the S^T half
+    // step/2 (which holds key 8*(r/4) + 4*hh + r%4 of that half).
+    auto stage_a = [&](int e) {
+      const int st = e >> 3, r = 8 * (st & 1) + (e & 7);
+      px[e] = __builtin_fmaf(scur[st >> 1][r], sl2, nb);
+    };
+    auto stage_b = [&](int e) { px[e] = fast_exp2(px[e]); };
+    auto stage_c = [&](int e) {
+      rs += px[e];
+      if (e & 1) pw[e >> 3][(e & 7) >> 1] = pack2<TT>(px[e - 1], px[e]);
     };
     __builtin_amdgcn_sched_barrier(0);
     read_k(0);
     read_k(1);
     __builtin_amdgcn_sched_barrier(0);
+    static_for<NSLOT + 2>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      constexpr int grp_id = i / G, m = i % G;
+      constexpr int q_of[9] = {0, 1, -1, 2, -1, 3, -1, -1, -1};
+      constexpr int p_of[9] = {-1, -1, 0, -1, 1, -1, 2, 3, -1};
+      if constexpr (i < NSLOT) {
+        if constexpr (m == 0) {  // operands two groups ahead
+          if constexpr (grp_id == 0) read_v(0);
+          if constexpr (grp_id == 1) read_k(2);
+          if constexpr (grp_id == 2) read_v(1);
+          if constexpr (grp_id == 3) read_k(3);
+          if constexpr (grp_id == 4) read_v(2);
+          if constexpr (grp_id == 5) read_v(3);
+        }
+        if constexpr (q_of[grp_id] >= 0) {
+          constexpr int q = q_of[grp_id];
+          const f32x16 acc = (m == 0 && (q & 1) == 0) ? f32x16{} : snext[q >> 1];
+          snext[q >> 1] = TT::mfma32(kop[q][m], qf[(q & 1) * G + m], acc);
+        } else {
+          constexpr int st = p_of[grp_id];
+          const V8 pf = __builtin_bit_cast(V8, make_uint4(pw[st][0], pw[st][1], pw[st][2], pw[st][3]));
+          oacc[m] = TT::mfma32(vop[st][m], pf, oacc[m]);
+        }
+      }
+      // probability stages: elements started at slot i-2 finish, at i-1 exp, at i start
+      static_for<32>([&](auto ec) {
+        constexpr int e = decltype(ec)::value;
+        constexpr int sa = (e * SA) / 32;  // slot of stage A
+        if constexpr (sa + 2 == i) stage_c(e);
+        if constexpr (sa + 1 == i) stage_b(e);
+        if constexpr (sa == i) stage_a(e);
+      });
+      // next tile's row maximum: half 0 after Q1 (one slot later), half 1 after Q3
+      if constexpr (i > 2 * G && i < 6 * G) {
+        constexpr int r0 = (16 * (i - 2 * G - 1)) / (4 * G - 1), r1 = (16 * (i - 2 * G)) / (4 * G - 1);
 #pragma unroll
-    for (int i = 0; i < NSLOT; ++i) {
-      const int grp_id = i / G, m = i % G;
-      // order Q0 Q1 P0 Q2 P1 Q3 P2 P3: group -> (is_q, index)
-      const int q_of[8] = {0, 1, -1, 2, -1, 3, -1, -1};
-      const int p_of[8] = {-1, -1, 0, -1, 1, -1, 2, 3};
-      if (m == 0) {  // operands of the next group
-        if (grp_id == 0) read_v(0);
-        if (grp_id == 1) read_k(2);
-        if (grp_id == 2) read_v(1);
-        if (grp_id == 3) read_k(3);
-        if (grp_id == 4) read_v(2);
-        if (grp_id == 5) read_v(3);
+        for (int r = r0; r < r1; ++r) {
+          if (r & 1) mx_b = fmaxf(mx_b, snext[0][r]);
+          else mx_a = fmaxf(mx_a, snext[0][r]);
+        }
       }
-      if (q_of[grp_id] >= 0) {
-        const int q = q_of[grp_id];
-        const f32x16 acc = (m == 0 && (q & 1) == 0) ? f32x16{} : snext[q >> 1];
-        snext[q >> 1] = TT::mfma32(kop[q][m], qf[(q & 1) * G + m], acc);
-      } else {
-        const int st = p_of[grp_id];
-        const V8 pf = __builtin_bit_cast(V8, make_uint4(pw[st][0], pw[st][1], pw[st][2], pw[st][3]));
-        oacc[m] = TT::mfma32(vop[st][m], pf, oacc[m]);
-      }
-      if (i < NEXP) {
+      if constexpr (i > 6 * G && i <= NSLOT) {
+        constexpr int r0 = (16 * (i - 6 * G - 1)) / (2 * G), r1 = (16 * (i - 6 * G)) / (2 * G);
 #pragma unroll
-        for (int e = (32 * i) / NEXP; e < (32 * (i + 1)) / NEXP; ++e) prob(e);
+        for (int r = r0; r < r1; ++r) {
+          if (r & 1) mx_b = fmaxf(mx_b, snext[1][r]);
+          else mx_a = fmaxf(mx_a, snext[1][r]);
+        }
       }
-      // next tile's row maximum: half 0 once Q1 is done, half 1 once Q3 is
-      if (i >= 2 * G && i < 6 * G) {
-#pragma unroll
-        for (int r = (16 * (i - 2 * G)) / (4 * G); r < (16 * (i - 2 * G + 1)) / (4 * G); ++r)
-          mnext = fmaxf(mnext, snext[0][r]);
-      }
-      if (i >= 6 * G) {
-#pragma unroll
-        for (int r = (16 * (i - 6 * G)) / (2 * G); r < (16 * (i - 6 * G + 1)) / (2 * G); ++r)
-          mnext = fmaxf(mnext, snext[1][r]);
-      }
-      if (i == NSLOT - 1) mnext = max_xor32(mnext);
       __builtin_amdgcn_sched_barrier(0);
-    }
+    });
+    const float mnext = max_xor32(fmaxf(mx_a, mx_b));
     l_run += rs;
     mx_cur = mnext;
     if (!tile_full(t + 1)) {
