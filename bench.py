@@ -60,18 +60,93 @@ def decode_bytes(ctx, Hq, Hkv, D, esize=2):
     return kv + S * Hq * D * esize * 2 + S * Hq * 4 + 4 * int((-(-ctx // 16)).sum()) + 4 * S
 
 
-def traffic_record(kernel_src):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    if not os.path.exists(path):
+FWD_SOURCES = [os.path.join(ROOT, "transformer_attention_09_amd", "csrc", f)
+               for f in ("fwd.hip", "common.h", "internal.h")]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_fwd_kernel_gqa8k_causal.txt")
+CALIB_BYTES = 512 << 20   # read, and written, by the calibration multiply
+
+
+def sources_sha256(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_record():
+    """HBM bytes per forward launch from the committed rocprofv3 counter
+    summary, if it was taken on the current forward kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
         return None
-    with open(path) as f:
-        rec = json.load(f)
-    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
-    if rec.get("source_sha256") != sha:
+    rec = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#") and not line.startswith(" "):
+                key, val = line.split(":", 1)
+                rec[key.strip()] = val.strip()
+    if rec.get("source_sha256") != sources_sha256(FWD_SOURCES):
         return None
-    return rec
+    try:
+        return {"workload": rec["workload"], "fetch_bytes": float(rec["fetch_bytes_per_launch"]),
+                "write_bytes": float(rec["write_bytes_per_launch"])}
+    except (KeyError, ValueError):
+        return None
+
+
+def write_traffic_record(fetch_csv, write_csv, command):
+    """Reduce two rocprofv3 --pmc counter tables (FETCH_SIZE, then WRITE_SIZE,
+    both in KiB per dispatch) of a `--copy-calibration` bench run to HBM bytes
+    per launch.  Each counter is scaled by the factor that maps its reading on
+    the calibration multiply (CALIB_BYTES read and CALIB_BYTES written) to
+    those known byte counts."""
+    import csv
+    import collections
+
+    def per_kernel(path, counter):
+        vals = collections.defaultdict(list)
+        per = collections.defaultdict(float)
+        names = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                per[r["Dispatch_Id"]] += float(r["Counter_Value"])
+                names[r["Dispatch_Id"]] = r["Kernel_Name"]
+        for d, v in per.items():
+            vals[names[d]].append(v)
+        return vals
+
+    def pick(vals, key):
+        hits = [k for k in vals if key in k and "FillFunctor" not in k]
+        if not hits:
+            raise SystemExit(f"no dispatch of a kernel matching {key!r}")
+        return hits[0], vals[hits[0]]
+
+    out = ["# HBM traffic per launch from rocprofv3 --pmc (FETCH_SIZE and WRITE_SIZE, KiB per dispatch),",
+           "# each scaled by its reading on an elementwise multiply that reads and writes 512 MiB.",
+           f"workload: gqa8k_causal",
+           f"source_sha256: {sources_sha256(FWD_SOURCES)}"]
+    for counter, path, tag in (("FETCH_SIZE", fetch_csv, "fetch"), ("WRITE_SIZE", write_csv, "write")):
+        vals = per_kernel(path, counter)
+        cname, cv = pick(vals, "elementwise")   # the multiply (the fill before it only writes)
+        scale = (CALIB_BYTES / 1024.0) / cv[0]
+        out.append(f"{tag}_calibration_kernel: {cname[:80]}")
+        out.append(f"{tag}_calibration_kib: {cv[0]:.1f} (expected {CALIB_BYTES / 1024:.0f})")
+        out.append(f"{tag}_scale: {scale:.4f}")
+        for key in ("fwd_kernel", "decode_split_kernel", "decode_combine_kernel"):
+            kname, kv = pick(vals, key)
+            avg = sum(kv) / len(kv)
+            label = {"fwd_kernel": "", "decode_split_kernel": "decode_split_",
+                     "decode_combine_kernel": "decode_combine_"}[key]
+            out.append(f"{label}{tag}_kib_per_dispatch_raw: {avg:.1f} over {len(kv)} dispatches")
+            out.append(f"{label}{tag}_bytes_per_launch: {avg * 1024 * scale:.0f}")
+    out.append("commands:")
+    for c in command:
+        out.append("  " + c)
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
 
 
 def cpu_baseline(cfg, target_s=20.0):
@@ -117,9 +192,16 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-detail", action="store_true", help="skip the extra per-workload numbers")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="first run one 512 MiB device-to-device copy, a dispatch of known traffic for "
-                         "scaling rocprofv3 FETCH_SIZE/WRITE_SIZE readings")
+                    help="first run one elementwise multiply that reads and writes 512 MiB, a dispatch of "
+                         "known traffic for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE readings")
+    ap.add_argument("--traffic-record", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the HBM traffic record from two rocprofv3 counter tables and exit (no GPU)")
+    ap.add_argument("--traffic-command", action="append", default=[],
+                    help="command line to note in the traffic record (repeatable)")
     args = ap.parse_args()
+    if args.traffic_record:
+        write_traffic_record(args.traffic_record[0], args.traffic_record[1], args.traffic_command)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path shards with no exchange over batch/KV-head groups or sequences; "
@@ -138,9 +220,9 @@ def main():
     stream = torch.cuda.current_stream()
 
     if args.copy_calibration:
-        src = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
+        src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
-        dst.copy_(src)
+        torch.mul(src, 2.0, out=dst)
         torch.cuda.synchronize()
         del src, dst
 
@@ -198,8 +280,7 @@ def main():
     log(f"decode: {d_ms * 1e3:.1f} us/call (split + combine), {d_gbs:.0f} GB/s "
         f"({100 * d_gbs / PEAK_HBM_GBS:.1f}% of peak), {n_rep} KV replicas")
 
-    fwd_src = os.path.join(ROOT, "transformer_attention_09_amd", "csrc", "fwd.hip")
-    trec = traffic_record(fwd_src)
+    trec = traffic_record()
     traffic = None
     if trec is not None and trec.get("workload") == fcfg.name:
         traffic = trec["fetch_bytes"] + trec["write_bytes"]
