@@ -295,6 +295,19 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     constexpr int P = decltype(par)::value;
     const E* kn = P ? kt0 : kt1;  // K(t+1)
     const E* vc = P ? vt1 : vt0;  // V(t)
+    constexpr int G = C::DB;         // MFMAs per group (KSTEPS/2 == D/32)
+    V8 kop[4][G];
+    auto read_k = [&](int q) {
+#pragma unroll
+      for (int k = 0; k < G; ++k) kop[q][k] = *(const V8*)(kn + koff[(q & 1) * G + k] + (q >> 1) * 32 * D);
+    };
+    // The first K operands go first: their LDS latency then overlaps the
+    // loads issued next and the rescale test instead of stalling the first
+    // MFMA.  (K(t+1) was completed before the barrier; the loads below fill
+    // the other buffers.)
+    read_k(0);
+    read_k(1);
+    __builtin_amdgcn_sched_barrier(0);
     load_k(t + 2, P ? kt1 : kt0);
     load_v(t + 1, P ? vt0 : vt1);
 
@@ -327,7 +340,6 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     // chains) follows its Q groups.  Each group's LDS operands are read two
     // groups ahead; sched_barrier keeps every MFMA in its own scheduling
     // region.
-    constexpr int G = C::DB;         // MFMAs per group (KSTEPS/2 == D/32)
     constexpr int NSLOT = 8 * G;     // MFMAs per tile
     constexpr int SA = G == 4 ? 26 : 9;  // slots that start a probability
     static_assert(C::KSTEPS / 2 == G && (G == 4 || G == 2), "Q and P groups have the same size");
@@ -335,11 +347,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     float rs = 0.f, mx_a = -INFINITY, mx_b = -INFINITY;
     float px[32];  // probabilities in flight: exponent argument, then value
     uint32_t pw[4][4];
-    V8 kop[4][G], vop[4][G];
-    auto read_k = [&](int q) {
-#pragma unroll
-      for (int k = 0; k < G; ++k) kop[q][k] = *(const V8*)(kn + koff[(q & 1) * G + k] + (q >> 1) * 32 * D);
-    };
+    V8 vop[4][G];
     auto read_v = [&](int st) {
 #pragma unroll
       for (int d = 0; d < G; ++d) {
@@ -356,17 +364,22 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     auto stage_b = [&](int e) { px[e] = fast_exp2(px[e]); };
     auto stage_c = [&](int e) {
       rs += px[e];
+      // keep the sum here, between the MFMAs, instead of letting it sink
+      // below the loop's barrier where nothing overlaps it
+      asm volatile("" : "+v"(rs));
       if (e & 1) pw[e >> 3][(e & 7) >> 1] = pack2<TT>(px[e - 1], px[e]);
     };
-    __builtin_amdgcn_sched_barrier(0);
-    read_k(0);
-    read_k(1);
     __builtin_amdgcn_sched_barrier(0);
     static_for<NSLOT + 2>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
       constexpr int grp_id = i / G, m = i % G;
       constexpr int q_of[9] = {0, 1, -1, 2, -1, 3, -1, -1, -1};
       constexpr int p_of[9] = {-1, -1, 0, -1, 1, -1, 2, 3, -1};
+      // From the first P.V group to the barrier this wave outranks the other
+      // work-group's wave on its SIMD that is still early in its tile: the
+      // four waves of a work-group then reach the barrier closer together,
+      // and the early wave has slack to give.
+      if constexpr (i == 2 * G) __builtin_amdgcn_s_setprio(1);
       if constexpr (i < NSLOT) {
         if constexpr (m == 0) {  // operands two groups ahead
           if constexpr (grp_id == 0) read_v(0);
@@ -425,6 +438,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     scur[1] = snext[1];
     wait_vmem();
     __syncthreads();
+    __builtin_amdgcn_s_setprio(0);
   };
 
   if (t_lo < t_hi) {
