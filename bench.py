@@ -11,7 +11,11 @@ stream; the decode's HBM GB/s is reported beside it.  The decode rotates
 through KV-pool replicas totalling >= 1 GiB so no timed call finds its K/V in
 the 256 MB last-level cache.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-detail]
+The decode is also compared with a plain streaming read of 2 GiB on the same
+device (attn_hbm_read_probe), the attainable HBM rate, and the shader clock is
+sampled with rocm-smi while a batch of forward launches runs.
+
+    python bench.py [--gpus 1] [--steps K=100] [--warmup W=10] [--no-cpu] [--no-detail]
 
 Prints exactly one JSON line on stdout.
 """
@@ -184,11 +188,43 @@ def cpu_baseline(cfg, target_s=20.0):
             "seconds": t}
 
 
+def read_ceiling(ta, torch, dev, stream, nbytes=2 << 30, reps=5):
+    """Attainable HBM read rate on this device: one plain streaming read of a
+    2 GiB buffer (attn_hbm_read_probe), averaged over a few back-to-back runs."""
+    buf = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        ta.attn_hbm_read_probe(buf, sink, stream=stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        ta.attn_hbm_read_probe(buf, sink, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del buf
+    return nbytes / (ms * 1e-3) / 1e9
+
+
+def sclk_under_load(run_batch):
+    """Shader clock (MHz) reported by rocm-smi while a batch of forward launches
+    is running; None if the tool is not available."""
+    import re
+    import subprocess
+    run_batch()
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=60)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    m = re.search(r"sclk clock level:\s*\d+:\s*\((\d+)\s*Mhz\)", r.stdout)
+    return int(m.group(1)) if m else None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-detail", action="store_true", help="skip the extra per-workload numbers")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -271,8 +307,10 @@ def main():
         step(args.warmup + i, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    f_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    d_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    f_all = [e[0].elapsed_time(e[1]) for e in evs]
+    d_all = [e[1].elapsed_time(e[2]) for e in evs]
+    f_ms, d_ms = float(np.mean(f_all)), float(np.mean(d_all))
+    f_med, d_med = float(np.median(f_all)), float(np.median(d_all))
     f_tflops = f_flops / (f_ms * 1e-3) / 1e12
     d_gbs = d_bytes / (d_ms * 1e-3) / 1e9
     log(f"forward {fcfg.name}: {f_ms * 1e3:.1f} us/launch, {f_tflops:.1f} TFLOP/s "
@@ -281,6 +319,18 @@ def main():
         f"({100 * d_gbs / PEAK_HBM_GBS:.1f}% of peak), {n_rep} KV replicas")
 
     trec = traffic_record()
+
+    # shader clock while the forward runs (a batch of about 0.5 s of launches)
+    n_batch = max(1, int(500.0 / max(f_ms, 1e-3)))
+
+    def fwd_batch():
+        for _ in range(n_batch):
+            ta.attn_fwd(q, k, v, out=out, lse=lse, scale=fcfg.scale, causal=True, stream=stream)
+
+    sclk = sclk_under_load(fwd_batch)
+    torch.cuda.synchronize()
+    ceiling = read_ceiling(ta, torch, dev, stream)
+    log(f"plain streaming read of 2 GiB: {ceiling:.0f} GB/s; shader clock under forward load: {sclk} MHz")
     traffic = None
     if trec is not None and trec.get("workload") == fcfg.name:
         traffic = trec["fetch_bytes"] + trec["write_bytes"]
@@ -314,6 +364,8 @@ def main():
             "traffic": traffic,
             "kernel": "fwd_kernel<BF16,128>",
             "avg_launch_us": round(f_ms * 1e3, 2),
+            "median_launch_us": round(f_med * 1e3, 2),
+            "sclk_mhz_under_load": sclk,
         },
         "decode": {
             "value": round(d_gbs, 1),
@@ -322,7 +374,10 @@ def main():
             "peak": PEAK_HBM_GBS,
             "frac": round(d_gbs / PEAK_HBM_GBS, 4),
             "avg_call_us": round(d_ms * 1e3, 2),
+            "median_call_us": round(d_med * 1e3, 2),
             "kv_replicas": n_rep,
+            "read_ceiling_GBs": round(ceiling, 1),
+            "frac_of_read_ceiling": round(d_gbs / ceiling, 4),
         },
     }
 
@@ -344,7 +399,7 @@ def main():
             torch.cuda.synchronize()
             return e0.elapsed_time(e1) / iters
 
-        for name in ("gqa8k_window", "std2048", "std2048_causal", "std512", "vit"):
+        for name in ("gqa8k_window", "std2048", "std2048_causal", "std512", "std512_causal", "vit", "tiny"):
             cfg = CONFIGS[name]
             ms = time_fwd(cfg)
             if cfg.window >= 0:
@@ -356,6 +411,9 @@ def main():
             detail[name] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(fl / ms / 1e9, 1),
                             "frac_mfma": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
                             "GB/s": round(byts / ms / 1e6, 1)}
+            # attainable roofline min(MFMA peak, AI x HBM peak)
+            attain = min(PEAK_BF16_TFLOPS, fl / byts * PEAK_HBM_GBS / 1e3)
+            detail[name]["frac_attainable"] = round(fl / ms / 1e9 / attain, 4)
             log(f"detail {name}: {detail[name]}")
         result["detail"] = detail
 

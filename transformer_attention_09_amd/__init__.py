@@ -8,6 +8,7 @@ the C ABI declared in include/attn.h, with the same entry-point names:
     attn_decode_paged(q, k_cache, ...)      q [S,Hq,D], caches [N,16,Hkv,D]
     attn_decode_paged_workspace_size(...)
     attn_status_string(status)
+    attn_hbm_read_probe(buf, sink)          plain streaming read (include/attn_measure.h)
 
 There is no fallback: if the library is missing or the device is not a
 gfx950 GPU the calls raise.  Build the library with
@@ -34,7 +35,8 @@ STATUS = {
     -6: "ATTN_ERR_DEVICE",
     -7: "ATTN_ERR_HIP",
 }
-EXPORTED = ("attn_fwd", "attn_decode_paged", "attn_decode_paged_workspace_size", "attn_status_string")
+EXPORTED = ("attn_fwd", "attn_decode_paged", "attn_decode_paged_workspace_size", "attn_status_string",
+            "attn_hbm_read_probe")
 
 _lib = None
 _lock = threading.Lock()
@@ -65,6 +67,8 @@ def load_library() -> ctypes.CDLL:
             lib.attn_decode_paged_workspace_size.restype = sz
             lib.attn_status_string.argtypes = [i32]
             lib.attn_status_string.restype = ctypes.c_char_p
+            lib.attn_hbm_read_probe.argtypes = [vp, sz, vp, vp]
+            lib.attn_hbm_read_probe.restype = i32
             _lib = lib
     return _lib
 
@@ -203,3 +207,17 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, ctx_lens, out=None, lse=
     if st != 0:
         raise AttnError(st, "attn_decode_paged")
     return out, lse
+
+
+def attn_hbm_read_probe(buf, sink, stream=None) -> None:
+    """Read the whole device tensor `buf` once (a plain streaming read, the
+    attainable-bandwidth reference for the HBM-bound decode).  `sink` is a
+    device tensor of at least 4 bytes that the kernel may write."""
+    _require_cuda("buf", buf)
+    _require_cuda("sink", sink)
+    if sink.numel() * sink.element_size() < 4:
+        raise ValueError("sink must hold at least 4 bytes")
+    st = load_library().attn_hbm_read_probe(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(),
+                                            _stream_handle(stream))
+    if st != 0:
+        raise AttnError(st, "attn_hbm_read_probe")

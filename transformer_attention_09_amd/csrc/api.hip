@@ -8,6 +8,7 @@
 #include <cstring>
 
 #include "../../include/attn.h"
+#include "../../include/attn_measure.h"
 #include "internal.h"
 
 #define ATTN_API extern "C" __attribute__((visibility("default")))
@@ -186,4 +187,15 @@ ATTN_API int attn_decode_paged(const void* q, const void* k_cache, const void* v
     if (e != hipSuccess) return ATTN_ERR_HIP;
   }
   return ATTN_OK;
+}
+
+ATTN_API int attn_hbm_read_probe(const void* p, size_t bytes, unsigned int* sink, void* stream) {
+  if (!p || !sink) return ATTN_ERR_NULL;
+  if (bytes < 16 || bytes % 16 != 0) return ATTN_ERR_SHAPE;
+  if (!aligned(p, 16)) return ATTN_ERR_ALIGN;
+  int cus = 1;
+  const int dev = check_device(&cus);
+  if (dev != ATTN_OK) return dev;
+  const hipError_t e = attn::launch_hbm_read(p, bytes, sink, cus, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }

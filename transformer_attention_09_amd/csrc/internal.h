@@ -55,5 +55,6 @@ constexpr int kDecodeWavesPerCU = 4;
 
 hipError_t launch_fwd(const FwdArgs& a, int D, int dtype, hipStream_t stream);
 hipError_t launch_decode(const DecArgs& a, int D, int dtype, hipStream_t stream);
+hipError_t launch_hbm_read(const void* p, size_t bytes, unsigned* sink, int cus, hipStream_t stream);
 
 }  // namespace attn
