@@ -5,6 +5,8 @@ One step = one pass of the whole hot path over resident synthetic inputs:
     L=8192, D=128, bf16, causal), and
   * the paged decode (64 sequences, Hq=12, Hkv=2, D=128, bf16, context
     lengths uniform in [512, 4096], 16-token blocks, permuted block table).
+The per-workload detail also times the paged prefill (16 sequences of 512 new
+tokens over paged contexts of 512-4096 tokens, same model shape).
 `value` is the forward's throughput in TFLOP/s (4*B*Hq*Lq*Lk*D, halved for
 causal), averaged over the timed launches with HIP events on the launch
 stream; the decode's HBM GB/s is reported beside it.  The decode rotates
@@ -248,7 +250,7 @@ def main():
     import torch
 
     import transformer_attention_09_amd as ta
-    from workloads import CONFIGS, dense_inputs, paged_inputs
+    from workloads import CONFIGS, dense_inputs, paged_inputs, prefill_inputs
 
     torch.cuda.set_device(0)
     ta.load_library()
@@ -415,6 +417,39 @@ def main():
             attain = min(PEAK_BF16_TFLOPS, fl / byts * PEAK_HBM_GBS / 1e3)
             detail[name]["frac_attainable"] = round(fl / ms / 1e9 / attain, 4)
             log(f"detail {name}: {detail[name]}")
+        # paged prefill: 512 new tokens per sequence over paged contexts
+        pcfg = CONFIGS["paged_prefill"]
+        pin = prefill_inputs(pcfg)
+        pq, pkc, pvc, pbt, pcl = (t.to(dev) for t in (pin.q, pin.k_cache, pin.v_cache, pin.block_table,
+                                                      pin.ctx_lens))
+        pout = torch.empty_like(pq)
+        plse = torch.empty((pcfg.B, pcfg.Hq, pcfg.Lq), dtype=torch.float32, device=dev)
+
+        def prefill():
+            ta.attn_fwd_paged(pq, pkc, pvc, pbt, pcl, out=pout, lse=plse, scale=pcfg.scale, causal=pcfg.causal,
+                              stream=stream)
+
+        for _ in range(3):
+            prefill()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            prefill()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 10
+        ctx = pin.ctx_lens.numpy().astype(np.int64)
+        i = np.arange(pcfg.Lq)
+        pairs = int(sum(np.clip(c - pcfg.Lq + i + 1, 0, c).sum() for c in ctx))
+        fl = 4.0 * pcfg.Hq * pcfg.D * pairs
+        byts = (2 * pcfg.B * pcfg.Lq * pcfg.Hq * pcfg.D * 2 + pcfg.B * pcfg.Hq * pcfg.Lq * 4
+                + int(ctx.sum()) * pcfg.Hkv * pcfg.D * 2 * 2)
+        attain = min(PEAK_BF16_TFLOPS, fl / byts * PEAK_HBM_GBS / 1e3)
+        detail["paged_prefill"] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(fl / ms / 1e9, 1),
+                                   "frac_mfma": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+                                   "GB/s": round(byts / ms / 1e6, 1),
+                                   "frac_attainable": round(fl / ms / 1e9 / attain, 4)}
+        log(f"detail paged_prefill: {detail['paged_prefill']}")
         result["detail"] = detail
 
     if not args.no_cpu:

@@ -127,6 +127,43 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                       float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * attn_fwd_paged - fused attention forward for Lq new query tokens per
+ * sequence over a paged KV cache (chunked / paged prefill).
+ *
+ *   q, out       [B, Lq, Hq, D]                          dtype
+ *   k_cache,
+ *   v_cache      [num_blocks, block_size, Hkv, D]         dtype
+ *   block_table  [B, max_blocks_per_seq]                  int32
+ *   ctx_lens     [B]                                      int32
+ *   lse          [B, Hq, Lq]  fp32, may be NULL
+ *
+ * The FlashAttention forward of a (long) prefill, with keys and values
+ * addressed through the paged cache's block table (the-ai.news article,
+ * section "Внимание типа FlashAttention и постраничное внимание": blockwise
+ * attention for prefill; a block table maps logical positions to physical
+ * blocks and the kernel translates every position through it).  Sequence b
+ * has the keys at positions [0, ctx_lens[b]); position p lives in physical
+ * block block_table[b, p / block_size] at slot p % block_size.  Its Lq query
+ * rows are the last Lq positions, so the result equals attn_fwd on the
+ * gathered contiguous K/V with Lk = ctx_lens[b], including the bottom-right
+ * causal alignment, the window and the rows that see no key when
+ * ctx_lens[b] < Lq (out = 0, lse = -inf).
+ *
+ * block_table and ctx_lens are device memory: 0 <= ctx_lens[b] <=
+ * max_blocks_per_seq * block_size and entries in [0, num_blocks) are caller
+ * preconditions, as for attn_decode_paged (violations never make the kernel
+ * read outside the given buffers, but give unspecified values).  No workspace;
+ * B = 0 or Lq = 0 is a no-op (pointers may then be NULL).
+ * Errors: ATTN_ERR_NULL, ATTN_ERR_SHAPE, ATTN_ERR_UNSUPPORTED (D, dtype,
+ * block_size != 16), ATTN_ERR_ALIGN, ATTN_ERR_DEVICE, ATTN_ERR_HIP.
+ */
+int attn_fwd_paged(const void* q, const void* k_cache, const void* v_cache,
+                   const int32_t* block_table, const int32_t* ctx_lens, int block_size,
+                   void* out, float* lse,
+                   int B, int Hq, int Hkv, int Lq, int D, int max_blocks_per_seq, int num_blocks,
+                   float scale, int causal, int window, int dtype, void* stream);
+
+/*
  * Bytes of workspace attn_decode_paged needs for these sizes (a pure host
  * function; no device is touched).  Returns 0 when nothing needs a workspace
  * (num_seqs = 0) or when the arguments are invalid.

@@ -39,6 +39,7 @@ from .core import (  # noqa: F401
     decode_paged,
     gather_paged_kv,
     online_attention,
+    prefill_paged,
     row_softmax,
     split_merge_attention,
 )

@@ -213,3 +213,26 @@ def decode_paged(q, k_cache, v_cache, block_table, ctx_lens, block_size: int, sc
         out[s] = o[0, 0]
         lse[s] = ls[0, :, 0]
     return out, lse
+
+
+def prefill_paged(q, k_cache, v_cache, block_table, ctx_lens, block_size: int, scale: float,
+                  causal: bool = True, window: int = -1):
+    """Lq new query tokens per sequence against that sequence's paged context.
+
+    q [B,Lq,Hq,D]: the last Lq positions of each sequence, i.e. query i of
+    sequence b sits at position ctx_lens[b] - Lq + i (the causal diagonal is
+    aligned bottom-right, as for dense attention with Lk = ctx_lens[b]).
+    K/V of positions [0, ctx_lens[b]) come through the block table exactly as
+    for decode_paged; then this is plain attention.  Returns
+    (out [B,Lq,Hq,D], lse [B,Hq,Lq]) in float64.
+    """
+    q = _f64(q)
+    B, Lq, Hq, D = q.shape
+    out = np.zeros((B, Lq, Hq, D))
+    lse = np.full((B, Hq, Lq), -np.inf)
+    for b in range(B):
+        K, V = gather_paged_kv(k_cache, v_cache, block_table, ctx_lens, block_size, b)
+        o, ls = attention(q[b][None], K[None], V[None], scale, causal=causal, window=window)
+        out[b] = o[0]
+        lse[b] = ls[0]
+    return out, lse

@@ -140,5 +140,44 @@ def test_hbm_read_probe_validation(args, code):
 
 
 def test_hbm_read_probe_valid_args_without_gpu_report_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: valid arguments would launch on the fake address")
     lib = ta.load_library()
     assert lib.attn_hbm_read_probe(P, 1 << 20, P, None) == DEV
+
+
+def _fwd_paged(**kw):
+    a = dict(q=P, kc=P, vc=P, table=P, ctx=P, bs=16, out=P, lse=None, B=2, Hq=4, Hkv=2, Lq=8, D=64, mbps=4,
+             nblocks=8, scale=0.125, causal=1, window=-1, dtype=1)
+    a.update(kw)
+    lib = ta.load_library()
+    return lib.attn_fwd_paged(a["q"], a["kc"], a["vc"], a["table"], a["ctx"], a["bs"], a["out"], a["lse"],
+                              a["B"], a["Hq"], a["Hkv"], a["Lq"], a["D"], a["mbps"], a["nblocks"],
+                              a["scale"], a["causal"], a["window"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(kc=None), NULL), (dict(vc=None), NULL), (dict(table=None), NULL),
+    (dict(ctx=None), NULL), (dict(out=None), NULL),
+    (dict(B=-1), SHAPE), (dict(Lq=-1), SHAPE), (dict(Hq=0), SHAPE), (dict(Hkv=0), SHAPE),
+    (dict(Hq=3, Hkv=2), SHAPE), (dict(scale=float("inf")), SHAPE), (dict(scale=float("nan")), SHAPE),
+    (dict(mbps=0), SHAPE), (dict(nblocks=0), SHAPE), (dict(mbps=1 << 27), SHAPE),
+    (dict(D=96), UNSUP), (dict(dtype=2), UNSUP), (dict(bs=32), UNSUP),
+    (dict(q=P_MIS), ALIGN), (dict(kc=P_MIS), ALIGN), (dict(vc=P_MIS), ALIGN), (dict(out=P_MIS), ALIGN),
+    (dict(table=P + 2), ALIGN), (dict(ctx=P + 2), ALIGN), (dict(lse=P + 2), ALIGN),
+])
+def test_fwd_paged_validation(kw, code):
+    assert _fwd_paged(**kw) == code
+
+
+def test_fwd_paged_empty_is_noop():
+    assert _fwd_paged(B=0, q=None, kc=None, vc=None, table=None, ctx=None, out=None) == OK
+    assert _fwd_paged(Lq=0, q=None, out=None, kc=None, vc=None, table=None, ctx=None) == OK
+
+
+def test_fwd_paged_valid_args_without_gpu_report_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: valid arguments would launch on the fake address")
+    assert _fwd_paged() == DEV

@@ -15,7 +15,8 @@ import pytest
 import torch
 
 import oracle
-from workloads import CONFIGS, DTYPES, dense_inputs, paged_inputs, poison_unused_slots, random_dense
+from workloads import (CONFIGS, DTYPES, PrefillConfig, dense_inputs, paged_inputs, poison_unused_slots,
+                       prefill_inputs, random_dense)
 
 pytestmark = pytest.mark.gpu
 
@@ -339,3 +340,69 @@ def test_paged_deterministic_bitwise(gpu_lib):
     a, la = run_decode(gpu_lib, inp, cfg.scale)
     b, lb = run_decode(gpu_lib, inp, cfg.scale)
     assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+# ------------------------------------------------------------ paged prefill
+
+def run_prefill(gpu_lib, inp, scale, causal=True, window=-1):
+    q, kc, vc, bt, cl = dev(inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.ctx_lens)
+    out, lse = gpu_lib.attn_fwd_paged(q, kc, vc, bt, cl, scale=scale, causal=causal, window=window,
+                                      check_table=True)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def test_workload_paged_prefill(gpu_lib):
+    cfg = CONFIGS["paged_prefill"]
+    say("[case] workload paged_prefill")
+    inp = prefill_inputs(cfg)
+    out, lse = run_prefill(gpu_lib, inp, cfg.scale, cfg.causal)
+    ro, rl = oracle.prefill_paged(inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.ctx_lens, 16, cfg.scale,
+                                  cfg.causal)
+    check("paged_prefill", out, lse, ro, rl, cfg.dtype)
+
+
+def _gathered(inp, b):
+    """Contiguous K/V [1, ctx, Hkv, D] of sequence b (an index gather on the host)."""
+    c = int(inp.ctx_lens[b])
+    p = torch.arange(c)
+    blk = inp.block_table[b, (p // 16)].long()
+    return inp.k_cache[blk, p % 16][None], inp.v_cache[blk, p % 16][None]
+
+
+@pytest.mark.parametrize("window", [-1, 300])
+def test_paged_prefill_bitwise_equals_dense_kernel(gpu_lib, window):
+    """Paging moves K/V, nothing else: per sequence, the dense kernel on the
+    gathered K/V (Lk = ctx_len) produces the same bits."""
+    cfg = PrefillConfig("pp_bitwise", 6, 200, 8, 2, 128, "bf16", 1, 900, 16, True, 41)
+    say(f"[case] paged prefill bitwise vs dense, window {window}")
+    inp = prefill_inputs(cfg, ctx_lens=np.array([200, 201, 64, 900, 333, 17]))
+    out, lse = run_prefill(gpu_lib, inp, cfg.scale, True, window)
+    for b in range(cfg.B):
+        k, v = _gathered(inp, b)
+        od, ld = run_fwd(gpu_lib, inp.q[b:b + 1], k, v, cfg.scale, True, window)
+        assert torch.equal(out[b:b + 1], od), f"sequence {b}: output differs from the dense kernel"
+        assert torch.equal(lse[b:b + 1], ld), f"sequence {b}: lse differs from the dense kernel"
+
+
+PREFILL_CASES = [
+    # D, dtype, Hq, Hkv, Lq, ctx_lens, causal, window
+    (64, "fp16", 4, 2, 70, [1, 15, 16, 17, 63, 64, 65, 200], True, -1),
+    (128, "bf16", 8, 1, 130, [130, 131, 257, 500, 1000], True, 100),
+    (128, "fp16", 6, 3, 33, [33, 40, 700, 0], False, -1),
+    (64, "bf16", 2, 2, 256, [1, 128, 300, 1024], False, 50),
+    (128, "bf16", 12, 2, 1, [5, 4096, 16, 17], True, -1),
+    (64, "fp16", 4, 4, 129, [129, 128, 0, 2000], True, 0),
+]
+
+
+@pytest.mark.parametrize("case", range(len(PREFILL_CASES)))
+def test_paged_prefill_ragged(gpu_lib, case):
+    D, dtype, Hq, Hkv, Lq, ctx, causal, window = PREFILL_CASES[case]
+    cfg = PrefillConfig(f"pp{case}", len(ctx), Lq, Hq, Hkv, D, dtype, 0, max(max(ctx), 1), 16, causal, 50 + case)
+    say(f"[case] paged prefill {case}: D{D} {dtype} Hq{Hq} Hkv{Hkv} Lq{Lq} ctx{ctx} causal{causal} w{window}")
+    inp = poison_unused_slots(prefill_inputs(cfg, ctx_lens=np.array(ctx), extra_blocks=3))
+    out, lse = run_prefill(gpu_lib, inp, cfg.scale, causal, window)
+    ro, rl = oracle.prefill_paged(inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.ctx_lens, 16, cfg.scale,
+                                  causal, window)
+    check(f"paged prefill {case}", out, lse, ro, rl, dtype)

@@ -411,3 +411,58 @@ def test_rows_subset_matches_full():
     part = oracle.attention(q, k, v, 0.3, True, 6, rows=rows)
     np.testing.assert_array_equal(part[0], full[0][:, rows])
     np.testing.assert_array_equal(part[1], full[1][:, :, rows])
+
+
+# ---------------------------------------------------------------- P12: paged prefill
+
+@pytest.mark.parametrize("causal,window", [(True, -1), (True, 3), (False, -1), (False, 2)])
+def test_p12_paged_prefill_equals_dense_and_library(causal, window):
+    """NEWS: paging changes where K/V live, not which are attended; the new
+    Lq tokens are the last Lq positions of each sequence (bottom-right
+    diagonal).  Checked against the oracle's dense attention on the unscattered
+    K/V, against torch's CPU float64 SDPA with an explicit mask, and for
+    invariance to the physical block permutation.  Contexts shorter than Lq
+    leave the first rows without keys (out 0, lse -inf)."""
+    r = np.random.default_rng(31)
+    Hq, Hkv, D, bs, Lq = 4, 2, 8, 4, 5
+    ctx = [1, 3, 5, 9, 16]
+    B = len(ctx)
+    K = [r.standard_normal((c, Hkv, D)) for c in ctx]
+    V = [r.standard_normal((c, Hkv, D)) for c in ctx]
+    q = r.standard_normal((B, Lq, Hq, D))
+    sc = 0.3
+    outs = []
+    for perm_seed in (None, 32):
+        kc, vc, table = _scatter_to_pool(K, V, ctx, bs, perm_seed, Hkv, D)
+        o, l = oracle.prefill_paged(q, kc, vc, table, np.array(ctx), bs, sc, causal, window)
+        outs.append((o, l))
+        for b, c in enumerate(ctx):
+            ro, rl = oracle.attention(q[b][None], K[b][None], V[b][None], sc, causal, window)
+            np.testing.assert_allclose(o[b], ro[0], atol=TIGHT, rtol=0)
+            np.testing.assert_allclose(l[b], rl[0], atol=TIGHT, rtol=0)
+            empty = ~np.isfinite(l[b])  # [Hq, Lq]
+            if causal:
+                # exactly the rows before the context starts are empty
+                assert np.array_equal(empty[0], np.arange(Lq) < Lq - c)
+            assert np.all(o[b].transpose(1, 0, 2)[empty] == 0)
+            rows = np.where(~empty[0])[0]
+            if len(rows):
+                sc32 = float(np.float32(sc))  # the oracle uses the float32 scale a kernel receives
+                lib = _torch_sdpa(q[b][None], K[b][None], V[b][None], sc32, causal, window)[0]
+                np.testing.assert_allclose(o[b][rows], lib[rows], atol=1e-12, rtol=0)
+    np.testing.assert_array_equal(outs[0][0], outs[1][0])
+    np.testing.assert_array_equal(outs[0][1], outs[1][1])
+
+
+def test_p12_paged_prefill_single_token_is_decode():
+    r = np.random.default_rng(33)
+    Hq, Hkv, D, bs = 6, 2, 8, 4
+    ctx = [2, 7, 12]
+    K = [r.standard_normal((c, Hkv, D)) for c in ctx]
+    V = [r.standard_normal((c, Hkv, D)) for c in ctx]
+    kc, vc, table = _scatter_to_pool(K, V, ctx, bs, 34, Hkv, D)
+    q = r.standard_normal((len(ctx), 1, Hq, D))
+    o, l = oracle.prefill_paged(q, kc, vc, table, np.array(ctx), bs, 0.4)
+    od, ld = oracle.decode_paged(q[:, 0], kc, vc, table, np.array(ctx), bs, 0.4)
+    np.testing.assert_allclose(o[:, 0], od, atol=TIGHT, rtol=0)
+    np.testing.assert_allclose(l[:, :, 0], ld, atol=TIGHT, rtol=0)

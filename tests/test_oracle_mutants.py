@@ -8,6 +8,7 @@ import importlib
 import numpy as np
 import pytest
 
+import oracle
 import tests.test_oracle as T
 
 OA = importlib.import_module("oracle.core")
@@ -28,6 +29,9 @@ def _pins():
     yield "p8", lambda: T.test_p8_gqa_equals_mha_with_expanded_kv(4, 2)
     yield "p10", T.test_p10_paged_equals_dense_and_permutation_invariant
     yield "p11", lambda: [T.test_p11_library_sdpa_random_shapes(s) for s in range(6)]
+    yield "p12", lambda: [T.test_p12_paged_prefill_equals_dense_and_library(c, w) for c, w in
+                          ((True, -1), (True, 3), (False, -1), (False, 2))]
+    yield "p12_decode", T.test_p12_paged_prefill_single_token_is_decode
 
 
 def _failing_pins():
@@ -42,17 +46,25 @@ def _failing_pins():
 
 @contextlib.contextmanager
 def planted(attr, fn):
+    """Replace oracle.core.<attr> (and the package's re-export of it, which the
+    pins call directly) for the duration of the block."""
     old = getattr(OA, attr)
+    old_pkg = getattr(oracle, attr, None)
     setattr(OA, attr, fn)
+    if old_pkg is not None:
+        setattr(oracle, attr, fn)
     try:
         yield
     finally:
         setattr(OA, attr, old)
+        if old_pkg is not None:
+            setattr(oracle, attr, old_pkg)
 
 
 _orig_mask = OA.allowed_mask
 _orig_softmax = OA.row_softmax
 _orig_gather = OA.gather_paged_kv
+_orig_prefill = OA.prefill_paged
 
 
 def _mask_strict_causal(Lq, Lk, causal, window, rows=None):
@@ -105,6 +117,14 @@ def _gather_ignores_table(k_cache, v_cache, block_table, ctx_lens, block_size, s
     return kc[blk, p % block_size], vc[blk, p % block_size]
 
 
+def _prefill_ignores_causal(q, kc, vc, table, ctx, bs, scale, causal=True, window=-1):
+    return _orig_prefill(q, kc, vc, table, ctx, bs, scale, False, window)
+
+
+def _prefill_drops_last_position(q, kc, vc, table, ctx, bs, scale, causal=True, window=-1):
+    return _orig_prefill(q, kc, vc, table, np.maximum(np.asarray(ctx) - 1, 0), bs, scale, causal, window)
+
+
 MUTANTS = {
     "gqa_modulo": ("kv_head", lambda h, Hq, Hkv: h % Hkv),
     "no_scale": ("scores", lambda qr, kr, sc: qr @ kr.T),
@@ -117,6 +137,8 @@ MUTANTS = {
     "softmax_of_negated": ("row_softmax", _softmax_neg),
     "unnormalised": ("row_softmax", _softmax_unnormalised),
     "gather_ignores_table": ("gather_paged_kv", _gather_ignores_table),
+    "prefill_ignores_causal": ("prefill_paged", _prefill_ignores_causal),
+    "prefill_drops_last_position": ("prefill_paged", _prefill_drops_last_position),
 }
 
 

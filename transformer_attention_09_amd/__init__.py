@@ -6,6 +6,7 @@ the C ABI declared in include/attn.h, with the same entry-point names:
 
     attn_fwd(q, k, v, ...)                  q [B,Lq,Hq,D], k/v [B,Lk,Hkv,D]
     attn_decode_paged(q, k_cache, ...)      q [S,Hq,D], caches [N,16,Hkv,D]
+    attn_fwd_paged(q, k_cache, ...)         q [B,Lq,Hq,D] over paged caches [N,16,Hkv,D]
     attn_decode_paged_workspace_size(...)
     attn_status_string(status)
     attn_hbm_read_probe(buf, sink)          plain streaming read (include/attn_measure.h)
@@ -36,7 +37,7 @@ STATUS = {
     -7: "ATTN_ERR_HIP",
 }
 EXPORTED = ("attn_fwd", "attn_decode_paged", "attn_decode_paged_workspace_size", "attn_status_string",
-            "attn_hbm_read_probe")
+            "attn_fwd_paged", "attn_hbm_read_probe")
 
 _lib = None
 _lock = threading.Lock()
@@ -67,6 +68,9 @@ def load_library() -> ctypes.CDLL:
             lib.attn_decode_paged_workspace_size.restype = sz
             lib.attn_status_string.argtypes = [i32]
             lib.attn_status_string.restype = ctypes.c_char_p
+            lib.attn_fwd_paged.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                           f32, i32, i32, i32, vp]
+            lib.attn_fwd_paged.restype = i32
             lib.attn_hbm_read_probe.argtypes = [vp, sz, vp, vp]
             lib.attn_hbm_read_probe.restype = i32
             _lib = lib
@@ -206,6 +210,71 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, ctx_lens, out=None, lse=
                                           ws_ptr, ws_bytes, _stream_handle(stream))
     if st != 0:
         raise AttnError(st, "attn_decode_paged")
+    return out, lse
+
+
+def _check_paged_table(block_table, ctx_lens, bs, num_blocks):
+    """Host-side check of the device-resident table and lengths (synchronises)."""
+    ctx = ctx_lens.cpu()
+    tab = block_table.cpu()
+    mbps = tab.shape[1]
+    if ctx.numel() and (int(ctx.min()) < 0 or int(ctx.max()) > mbps * bs):
+        raise ValueError("ctx_lens outside [0, max_blocks_per_seq * block_size]")
+    for s in range(tab.shape[0]):
+        n = -(-int(ctx[s]) // bs)
+        if n and (int(tab[s, :n].min()) < 0 or int(tab[s, :n].max()) >= num_blocks):
+            raise ValueError(f"block_table row {s} points outside the pool")
+
+
+def attn_fwd_paged(q, k_cache, v_cache, block_table, ctx_lens, out=None, lse=None,
+                   scale: Optional[float] = None, causal: bool = True, window: int = -1, stream=None,
+                   return_lse: bool = True, check_table: bool = False):
+    """Paged prefill; returns (out, lse).
+
+    q [B,Lq,Hq,D]: the last Lq positions of each sequence; k_cache/v_cache
+    [num_blocks, block_size, Hkv, D]; block_table int32 [B, max_blocks_per_seq];
+    ctx_lens int32 [B] (context lengths including the Lq new tokens).
+    check_table=True validates the table and lengths on the host first (it
+    synchronises; meant for tests).
+    """
+    import torch
+
+    for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("block_table", block_table),
+                 ("ctx_lens", ctx_lens)):
+        _require_cuda(n, t)
+    if q.dim() != 4 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("expected q [B,Lq,Hq,D] and caches [N,block_size,Hkv,D] of equal shape")
+    B, Lq, Hq, D = q.shape
+    num_blocks, bs, Hkv, Dk = k_cache.shape
+    if Dk != D or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("q and caches disagree in head dim or dtype")
+    if block_table.dtype != torch.int32 or ctx_lens.dtype != torch.int32:
+        raise ValueError("block_table and ctx_lens must be int32")
+    if block_table.dim() != 2 or block_table.shape[0] != B or ctx_lens.shape != (B,):
+        raise ValueError("block_table must be [B, max_blocks_per_seq] and ctx_lens [B]")
+    mbps = block_table.shape[1]
+    if check_table:
+        _check_paged_table(block_table, ctx_lens, bs, num_blocks)
+    if out is None:
+        out = torch.empty_like(q)
+    _require_cuda("out", out)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _require_cuda("lse", lse)
+        if lse.shape != (B, Hq, Lq) or lse.dtype != torch.float32:
+            raise ValueError("lse must be float32 [B,Hq,Lq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    st = load_library().attn_fwd_paged(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                       block_table.data_ptr(), ctx_lens.data_ptr(), bs,
+                                       out.data_ptr(), lse.data_ptr() if lse is not None else None,
+                                       B, Hq, Hkv, Lq, D, mbps, num_blocks, float(scale), int(bool(causal)),
+                                       int(window), _dtype_code(q), _stream_handle(stream))
+    if st != 0:
+        raise AttnError(st, "attn_fwd_paged")
     return out, lse
 
 

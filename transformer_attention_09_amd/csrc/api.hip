@@ -106,7 +106,52 @@ ATTN_API int attn_fwd(const void* q, const void* k, const void* v, void* out, fl
   a.window = window < 0 ? -1 : window;
   a.scale_log2 = scale * attn::kLog2e;
   a.n_qblocks = (int)n_qblocks;
+  a.block_table = nullptr;
+  a.ctx_lens = nullptr;
+  a.max_blocks_per_seq = 0;
+  a.num_blocks = 0;
   hipError_t e = attn::launch_fwd(a, D, dtype, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+ATTN_API int attn_fwd_paged(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_table, const int32_t* ctx_lens, int block_size,
+                            void* out, float* lse,
+                            int B, int Hq, int Hkv, int Lq, int D, int max_blocks_per_seq, int num_blocks,
+                            float scale, int causal, int window, int dtype, void* stream) {
+  if (B < 0 || Lq < 0 || Hq <= 0 || Hkv <= 0) return ATTN_ERR_SHAPE;
+  const bool empty = (B == 0 || Lq == 0);
+  if (!empty && (!q || !out || !k_cache || !v_cache || !block_table || !ctx_lens)) return ATTN_ERR_NULL;
+  if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+  if (!std::isfinite(scale)) return ATTN_ERR_SHAPE;
+  if (!supported_d(D) || !supported_dtype(dtype) || block_size != attn::kPagedBlock) return ATTN_ERR_UNSUPPORTED;
+  if (!empty && (max_blocks_per_seq <= 0 || num_blocks <= 0)) return ATTN_ERR_SHAPE;
+  if (!prod_ok(B, Lq, Hq, D) || !prod_ok(num_blocks, block_size, Hkv, D) || !prod_ok(B, max_blocks_per_seq, 1, 1))
+    return ATTN_ERR_SHAPE;
+  // the longest context must fit the kernel's 32-bit key positions
+  if ((long long)max_blocks_per_seq * block_size > 0x3fffffffLL) return ATTN_ERR_SHAPE;
+  const long long n_qblocks = ((long long)Lq + attn::kPrefillBlockM - 1) / attn::kPrefillBlockM;
+  if (n_qblocks * Hq * (long long)B > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16)) return ATTN_ERR_ALIGN;
+  if (!aligned(block_table, 4) || !aligned(ctx_lens, 4)) return ATTN_ERR_ALIGN;
+  if (lse && !aligned(lse, 4)) return ATTN_ERR_ALIGN;
+  if (empty) return ATTN_OK;
+  const int dev = check_device();
+  if (dev != ATTN_OK) return dev;
+
+  attn::FwdArgs a;
+  a.q = q; a.k = k_cache; a.v = v_cache; a.o = out; a.lse = lse;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Lq = Lq; a.Lk = 0;
+  a.group = Hq / Hkv;
+  a.causal = causal ? 1 : 0;
+  a.window = window < 0 ? -1 : window;
+  a.scale_log2 = scale * attn::kLog2e;
+  a.n_qblocks = (int)n_qblocks;
+  a.block_table = block_table;
+  a.ctx_lens = ctx_lens;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  hipError_t e = attn::launch_fwd_paged(a, D, dtype, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

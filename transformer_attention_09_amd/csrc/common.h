@@ -86,6 +86,9 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 __device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
+__device__ __forceinline__ int buf_load4(rsrc_t r, uint32_t byte_off) {
+  return (int)__builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0);
+}
 // Range-checked stores: a store outside [0, bytes) of its resource is dropped,
 // so a resource of size 0 turns a store into a no-op without a branch.
 typedef unsigned u32x4_t __attribute__((vector_size(16)));

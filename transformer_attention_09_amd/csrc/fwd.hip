@@ -105,7 +105,7 @@ struct Par {
   static constexpr int value = P;
 };
 
-template <typename TT, int D>
+template <typename TT, int D, bool PAGED>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   using C = FwdCfg<D>;
   using E = typename TT::elem;
@@ -145,14 +145,17 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   }
   const int b = gid / a.Hkv, g = gid % a.Hkv;
   const int hq = g * a.group + hj;
+  // Keys of batch row b: Lk of the dense layout, or the paged context length.
+  int Lk = a.Lk;
+  if constexpr (PAGED) Lk = min(max(a.ctx_lens[b], 0), a.max_blocks_per_seq * kPagedBlock);
   const int qb = a.causal ? (a.n_qblocks - 1 - qb_rank) : qb_rank;
   const int q0 = qb * C::BM;
-  const int off = a.Lk - a.Lq;  // bottom-right alignment of the causal diagonal
+  const int off = Lk - a.Lq;  // bottom-right alignment of the causal diagonal
   const int W = a.window;
 
   // ---- key-tile range of the whole work-group
   const int row_hi = min(q0 + C::BM, a.Lq) - 1;
-  int j_lo = 0, j_hi = a.Lk - 1;
+  int j_lo = 0, j_hi = Lk - 1;
   if (a.causal) j_hi = min(j_hi, row_hi + off);
   if (W >= 0) {
     j_lo = max(j_lo, q0 + off - W);
@@ -185,7 +188,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     }
   }
   // Keys this row may see: [jlo_row, jhi_row] (empty when jhi_row < jlo_row).
-  int jlo_row = 0, jhi_row = a.Lk - 1;
+  int jlo_row = 0, jhi_row = Lk - 1;
   if (a.causal) jhi_row = min(jhi_row, qi + off);
   if (W >= 0) {
     jlo_row = max(jlo_row, qi + off - W);
@@ -214,15 +217,28 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   constexpr int RPI = 1024 / (D * (int)sizeof(E));  // rows per instruction
   constexpr int IPW = C::BN / RPI / 4;              // instructions per wave per tile
   const size_t kv_rs = (size_t)a.Hkv * D;           // elements between consecutive keys
-  const E* kb = (const E*)a.k + ((size_t)b * a.Lk * a.Hkv + g) * D;
-  const E* vb = (const E*)a.v + ((size_t)b * a.Lk * a.Hkv + g) * D;
+  // Paged: the IPW*RPI = 16 tile rows of wave w are exactly one cache block,
+  // logical block (BN/16)*t + w of the sequence, so each load instruction
+  // addresses rows of one block and the wave needs one table entry per tile.
+  static_assert(!PAGED || IPW * RPI == kPagedBlock, "a wave's tile rows are one cache block");
+  const E* kb;
+  const E* vb;
+  if constexpr (PAGED) {
+    kb = (const E*)a.k + (size_t)g * D;
+    vb = (const E*)a.v + (size_t)g * D;
+  } else {
+    kb = (const E*)a.k + ((size_t)b * Lk * a.Hkv + g) * D;
+    vb = (const E*)a.v + ((size_t)b * Lk * a.Hkv + g) * D;
+  }
   uint32_t ksrc[IPW], vsrc[IPW];
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
-    const int r = (wave * IPW + i) * RPI + lane / C::CPR;
+    const int rw = i * RPI + lane / C::CPR;  // row among the wave's 16
+    const int r = wave * IPW * RPI + rw;     // row of the tile
     const int p = lane % C::CPR;
-    ksrc[i] = (uint32_t)(((size_t)r * kv_rs + ((p ^ k_swz<D>(r)) << 3)) * sizeof(E));
-    vsrc[i] = (uint32_t)(((size_t)r * kv_rs + ((p ^ v_swz<D>(r)) << 3)) * sizeof(E));
+    const size_t src_row = PAGED ? (size_t)rw : (size_t)r;
+    ksrc[i] = (uint32_t)((src_row * kv_rs + ((p ^ k_swz<D>(r)) << 3)) * sizeof(E));
+    vsrc[i] = (uint32_t)((src_row * kv_rs + ((p ^ v_swz<D>(r)) << 3)) * sizeof(E));
   }
   auto tile_bytes = [&](int t) -> uint32_t {
     // Resources start at the tile's first key and end after key Lk-1, so
@@ -230,24 +246,46 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     // an empty resource (the loads then only write zeros to a free buffer).
     if (t >= t_hi) return 0u;
     const size_t jt = (size_t)t * C::BN;
-    const size_t bytes = (((size_t)(a.Lk - jt) - 1) * kv_rs + D) * sizeof(E);
+    const size_t bytes = (((size_t)(Lk - jt) - 1) * kv_rs + D) * sizeof(E);
     return bytes > 0x7fffffffu ? 0x7fffffffu : (uint32_t)bytes;
   };
-  auto load_k = [&](int t, E* dst) {
-    const rsrc_t r = make_rsrc(kb + (size_t)t * C::BN * kv_rs, tile_bytes(t));
+  // Paged: the table row of sequence b (entries past its end read as 0) and
+  // the resource of this wave's block of tile t.  A block holding no visible
+  // key, or of a tile past the range, gets an empty resource.
+  const rsrc_t trow = make_rsrc(PAGED ? (const void*)(a.block_table + (size_t)b * a.max_blocks_per_seq) : a.q,
+                                PAGED ? (uint32_t)a.max_blocks_per_seq * 4u : 0u);
+  auto fetch_entry = [&](int t) -> int {  // a vector load, so it is counted with the tile loads
+    return buf_load4(trow, (uint32_t)(t * (C::BN / kPagedBlock) + wave) * 4u);
+  };
+  const size_t blk_elems = (size_t)kPagedBlock * kv_rs;
+  auto block_rsrc = [&](const E* base, int t, int entry) -> rsrc_t {
+    const int lb = t * (C::BN / kPagedBlock) + wave;
+    const int ntok = t < t_hi ? min(kPagedBlock, Lk - kPagedBlock * lb) : 0;
+    const int e = min(max(__builtin_amdgcn_readfirstlane(entry), 0), a.num_blocks - 1);
+    return make_rsrc(base + (size_t)e * blk_elems, ntok > 0 ? (uint32_t)(((ntok - 1) * kv_rs + D) * sizeof(E)) : 0u);
+  };
+  auto load_k = [&](int t, E* dst, int entry) {
+    rsrc_t r;
+    if constexpr (PAGED) r = block_rsrc(kb, t, entry);
+    else r = make_rsrc(kb + (size_t)t * C::BN * kv_rs, tile_bytes(t));
 #pragma unroll
     for (int i = 0; i < IPW; ++i) buf_load16_lds(r, ksrc[i], dst + (wave * IPW + i) * RPI * D);
   };
-  auto load_v = [&](int t, E* dst) {
-    const rsrc_t r = make_rsrc(vb + (size_t)t * C::BN * kv_rs, tile_bytes(t));
+  auto load_v = [&](int t, E* dst, int entry) {
+    rsrc_t r;
+    if constexpr (PAGED) r = block_rsrc(vb, t, entry);
+    else r = make_rsrc(vb + (size_t)t * C::BN * kv_rs, tile_bytes(t));
 #pragma unroll
     for (int i = 0; i < IPW; ++i) buf_load16_lds(r, vsrc[i], dst + (wave * IPW + i) * RPI * D);
   };
+  // Paged: table entries for the next K and V tile loads (K(t+2) and V(t+1)
+  // at tile t); each tile fetches the entry of K(t+3), one tile ahead of use.
+  int eK = 0, eV = 0;
 
   // Does every row of this wave see every key of tile t?  (Wave-uniform.)
   auto tile_full = [&](int t) {
     const int jt = t * C::BN;
-    return (jt + C::BN <= a.Lk) && (!a.causal || jt + C::BN - 1 <= wr_lo + off) &&
+    return (jt + C::BN <= Lk) && (!a.causal || jt + C::BN - 1 <= wr_lo + off) &&
            (W < 0 || jt >= wr_hi + off - W) && (W < 0 || a.causal || jt + C::BN - 1 <= wr_lo + off + W);
   };
   // Element-wise mask of tile t's scores: key (kh*32 + 8*(r/4) + 4*hh + r%4)
@@ -308,8 +346,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     read_k(0);
     read_k(1);
     __builtin_amdgcn_sched_barrier(0);
-    load_k(t + 2, P ? kt1 : kt0);
-    load_v(t + 1, P ? vt0 : vt1);
+    load_k(t + 2, P ? kt1 : kt0, eK);
+    load_v(t + 1, P ? vt0 : vt1, eV);
+    int eN = 0;
+    if constexpr (PAGED) eN = fetch_entry(t + 3);
 
     // Move the exponent base only when the maximum has grown by more than
     // the threshold somewhere in the wave; rescale those rows.
@@ -439,12 +479,25 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     wait_vmem();
     __syncthreads();
     __builtin_amdgcn_s_setprio(0);
+    if constexpr (PAGED) {
+      eV = eK;
+      eK = eN;
+    }
   };
 
   if (t_lo < t_hi) {
-    load_k(t_lo, kt0);
-    load_v(t_lo, vt0);
-    load_k(t_lo + 1, kt1);
+    if constexpr (PAGED) {
+      const int e0 = fetch_entry(t_lo), e1 = fetch_entry(t_lo + 1);
+      eK = fetch_entry(t_lo + 2);
+      eV = e1;
+      load_k(t_lo, kt0, e0);
+      load_v(t_lo, vt0, e0);
+      load_k(t_lo + 1, kt1, e1);
+    } else {
+      load_k(t_lo, kt0, 0);
+      load_v(t_lo, vt0, 0);
+      load_k(t_lo + 1, kt1, 0);
+    }
     wait_vmem();
     __syncthreads();
     scur[0] = f32x16{};
@@ -485,16 +538,23 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   }
 }
 
-template <typename TT, int D>
+template <typename TT, int D, bool PAGED>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   const long long blocks = (long long)a.n_qblocks * a.Hq * a.B;
-  hipLaunchKernelGGL((fwd_kernel<TT, D>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((fwd_kernel<TT, D, PAGED>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int D, int dtype, hipStream_t stream) {
-  if (dtype == 1) return D == 128 ? launch_fwd_t<BF16, 128>(a, stream) : launch_fwd_t<BF16, 64>(a, stream);
-  return D == 128 ? launch_fwd_t<F16, 128>(a, stream) : launch_fwd_t<F16, 64>(a, stream);
+  if (dtype == 1)
+    return D == 128 ? launch_fwd_t<BF16, 128, false>(a, stream) : launch_fwd_t<BF16, 64, false>(a, stream);
+  return D == 128 ? launch_fwd_t<F16, 128, false>(a, stream) : launch_fwd_t<F16, 64, false>(a, stream);
+}
+
+hipError_t launch_fwd_paged(const FwdArgs& a, int D, int dtype, hipStream_t stream) {
+  if (dtype == 1)
+    return D == 128 ? launch_fwd_t<BF16, 128, true>(a, stream) : launch_fwd_t<BF16, 64, true>(a, stream);
+  return D == 128 ? launch_fwd_t<F16, 128, true>(a, stream) : launch_fwd_t<F16, 64, true>(a, stream);
 }
 
 }  // namespace attn

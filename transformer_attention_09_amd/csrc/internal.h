@@ -19,6 +19,12 @@ struct FwdArgs {
   int window;      // < 0: none
   float scale_log2;  // scale * log2(e): scores are handled in base 2
   int n_qblocks;
+  // Paged K/V (attn_fwd_paged): k and v are caches [num_blocks, 16, Hkv, D],
+  // sequence b's keys are positions [0, ctx_lens[b]) behind block_table[b],
+  // and Lk is unused.  Null for the dense layout.
+  const int32_t* block_table;
+  const int32_t* ctx_lens;
+  int max_blocks_per_seq, num_blocks;
 };
 
 // Paged decode.  The cache blocks of all sequences, taken in sequence order,
@@ -45,6 +51,7 @@ struct DecArgs {
 };
 
 constexpr int kPrefillBlockM = 128;
+constexpr int kPagedBlock = 16;  // tokens per cache block (both paged entry points)
 constexpr float kLog2e = 1.44269504088896340736f;
 
 // Decode launch limits.  Larger batches are cut into several launches.
@@ -54,6 +61,7 @@ constexpr int kDecodeMaxStreams = 2048;
 constexpr int kDecodeWavesPerCU = 4;
 
 hipError_t launch_fwd(const FwdArgs& a, int D, int dtype, hipStream_t stream);
+hipError_t launch_fwd_paged(const FwdArgs& a, int D, int dtype, hipStream_t stream);
 hipError_t launch_decode(const DecArgs& a, int D, int dtype, hipStream_t stream);
 hipError_t launch_hbm_read(const void* p, size_t bytes, unsigned* sink, int cus, hipStream_t stream);
 

@@ -19,7 +19,9 @@ Recipe (identical for every consumer):
   * dense workloads draw q, k, v in that order as float32 standard normals
     and cast them to fp16/bf16 with round-to-nearest-even (torch's cast);
   * the paged workload draws ctx_lens (integers, inclusive range), then the
-    physical-block permutation, then q, then the K pool, then the V pool.
+    physical-block permutation, then q, then the K pool, then the V pool;
+  * the paged prefill workload (Lq new tokens per sequence, the last Lq
+    positions of its context) follows the same order, with q [B, Lq, Hq, D].
 """
 from __future__ import annotations
 
@@ -74,6 +76,32 @@ class PagedConfig:
         return -(-self.ctx_max // self.block_size)
 
 
+@dataclasses.dataclass(frozen=True)
+class PrefillConfig:
+    """Paged prefill: Lq new query tokens per sequence over a paged context of
+    ctx_lens[b] >= Lq positions (the new tokens are the last Lq of them)."""
+    name: str
+    B: int
+    Lq: int
+    Hq: int
+    Hkv: int
+    D: int
+    dtype: str
+    ctx_min: int
+    ctx_max: int  # inclusive
+    block_size: int
+    causal: bool
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return -(-self.ctx_max // self.block_size)
+
+
 # The five workloads.  Seeds: 1 tiny, 2/3 standard L=512/2048, 4 ViT,
 # 5 long GQA, 6 paged decode.
 CONFIGS = {
@@ -86,6 +114,8 @@ CONFIGS = {
     "gqa8k_causal": DenseConfig("gqa8k_causal", 1, 32, 8, 8192, 8192, 128, "bf16", True, -1, 5),
     "gqa8k_window": DenseConfig("gqa8k_window", 1, 32, 8, 8192, 8192, 128, "bf16", True, 4096, 5),
     "paged_decode": PagedConfig("paged_decode", 64, 12, 2, 128, "bf16", 512, 4096, 16, 6),
+    # chunked prefill on the same model shape: 512 new tokens per sequence
+    "paged_prefill": PrefillConfig("paged_prefill", 16, 512, 12, 2, 128, "bf16", 512, 4096, 16, True, 7),
 }
 
 
@@ -166,3 +196,30 @@ def poison_unused_slots(inp: PagedInputs, value: float = float("nan")) -> PagedI
     kc[~used] = value
     vc[~used] = value
     return dataclasses.replace(inp, k_cache=kc, v_cache=vc)
+
+
+def prefill_inputs(cfg: PrefillConfig, seed: Optional[int] = None, identity_perm: bool = False,
+                   ctx_lens: Optional[np.ndarray] = None, extra_blocks: int = 0) -> PagedInputs:
+    """Paged prefill inputs: a pool of sum(ceil(ctx/bs)) (+extra_blocks)
+    permuted blocks as in paged_inputs, and q [B, Lq, Hq, D]."""
+    rng = np.random.default_rng(cfg.seed if seed is None else seed)
+    if ctx_lens is None:
+        ctx = rng.integers(cfg.ctx_min, cfg.ctx_max + 1, size=cfg.B)
+    else:
+        ctx = np.asarray(ctx_lens, dtype=np.int64)
+        assert ctx.shape == (cfg.B,)
+    bs = cfg.block_size
+    nblk = -(-ctx // bs)
+    num_blocks = max(int(nblk.sum()) + extra_blocks, 1)
+    perm = np.arange(num_blocks) if identity_perm else rng.permutation(num_blocks)
+    mbps = max(cfg.max_blocks_per_seq, int(nblk.max()) if len(nblk) else 0, 1)
+    table = np.zeros((cfg.B, mbps), dtype=np.int32)
+    off = 0
+    for s in range(cfg.B):
+        table[s, : nblk[s]] = perm[off: off + nblk[s]]
+        off += nblk[s]
+    q = _normals(rng, (cfg.B, cfg.Lq, cfg.Hq, cfg.D), cfg.dtype)
+    kc = _normals(rng, (num_blocks, bs, cfg.Hkv, cfg.D), cfg.dtype)
+    vc = _normals(rng, (num_blocks, bs, cfg.Hkv, cfg.D), cfg.dtype)
+    return PagedInputs(q, kc, vc, torch.from_numpy(table), torch.from_numpy(ctx.astype(np.int32)),
+                       bs, num_blocks, mbps)
