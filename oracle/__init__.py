@@ -33,6 +33,7 @@ Parity status of every function here is recorded in tests/test_oracle.py
 """
 from .core import (  # noqa: F401
     allowed_mask,
+    attention_backward,
     kv_head,
     scores,
     attention,

@@ -236,3 +236,43 @@ def prefill_paged(q, k_cache, v_cache, block_table, ctx_lens, block_size: int, s
         out[b] = o[0]
         lse[b] = ls[0]
     return out, lse
+
+
+def attention_backward(q, k, v, dout, scale: float, causal: bool = False, window: int = -1):
+    """Gradients of L = sum(dout * attention(q, k, v)) with respect to q, k, v.
+
+    The chain rule applied to the definition ("Самовнимание, ядра CUDA и
+    FlashAttention", section 1; section 3 keeps only the normalisation
+    statistics and recomputes the tiles in the backward pass, which must give
+    these same values): with S = scale * Q K^T and P its row softmax over the
+    visible keys,
+        dV = P^T dO,   dP = dO V^T,
+        dS = P * (dP - sum_j P_ij dP_ij)     (the softmax Jacobian),
+        dQ = scale * dS K,   dK = scale * dS^T Q,
+    per (batch, query head); a K/V head's gradients sum over the query heads
+    that share it.  Rows without a visible key contribute nothing.
+    Returns (dq, dk, dv) in float64, shaped like q, k, v.
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, Lq, Hq, D = q.shape
+    Lk, Hkv = k.shape[1], k.shape[2]
+    assert k.shape == (B, Lk, Hkv, D) and v.shape == k.shape and do.shape == q.shape and Hq % Hkv == 0
+    sc = _scale64(scale)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for r0 in range(0, Lq, _ROW_CHUNK):
+        sel = np.arange(r0, min(Lq, r0 + _ROW_CHUNK))
+        ok = allowed_mask(Lq, Lk, causal, window, sel)
+        for b in range(B):
+            for h in range(Hq):
+                g = kv_head(h, Hq, Hkv)
+                S = scores(q[b, sel, h, :], k[b, :, g, :], sc)
+                P, _ = row_softmax(S, ok)
+                dO = do[b, sel, h, :]
+                dv[b, :, g, :] += P.T @ dO
+                dP = dO @ v[b, :, g, :].T
+                dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+                dq[b, sel, h, :] = sc * (dS @ k[b, :, g, :])
+                dk[b, :, g, :] += sc * (dS.T @ q[b, sel, h, :])
+    return dq, dk, dv

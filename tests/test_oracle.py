@@ -466,3 +466,111 @@ def test_p12_paged_prefill_single_token_is_decode():
     od, ld = oracle.decode_paged(q[:, 0], kc, vc, table, np.array(ctx), bs, 0.4)
     np.testing.assert_allclose(o[:, 0], od, atol=TIGHT, rtol=0)
     np.testing.assert_allclose(l[:, :, 0], ld, atol=TIGHT, rtol=0)
+
+
+# ---------------------------------------------------------------- P13: backward
+
+def _loss(q, k, v, do, sc, causal, window):
+    o, _ = oracle.attention(q, k, v, sc, causal, window)
+    return float((o * do).sum())
+
+
+@pytest.mark.parametrize("causal,window", [(False, -1), (True, -1), (True, 1), (False, 1)])
+def test_p13_backward_matches_finite_differences(causal, window):
+    """Central differences of L = sum(dO * attention) on a tiny GQA case
+    (3 query rows, 4 keys; the last row of the causal case sees all keys)."""
+    r = np.random.default_rng(61)
+    B, Hq, Hkv, Lq, Lk, D = 1, 2, 1, 3, 4, 3
+    q = r.standard_normal((B, Lq, Hq, D))
+    k = r.standard_normal((B, Lk, Hkv, D))
+    v = r.standard_normal((B, Lk, Hkv, D))
+    do = r.standard_normal((B, Lq, Hq, D))
+    sc = 0.5  # exactly representable in float32
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, sc, causal, window)
+    eps = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args_p = {"q": q, "k": k, "v": v}
+            args_m = dict(args_p)
+            args_p[name], args_m[name] = xp, xm
+            num[idx] = (_loss(args_p["q"], args_p["k"], args_p["v"], do, sc, causal, window)
+                        - _loss(args_m["q"], args_m["k"], args_m["v"], do, sc, causal, window)) / (2 * eps)
+        np.testing.assert_allclose(g, num, atol=1e-7, rtol=0, err_msg=f"d{name}")
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_p13_backward_matches_torch_autograd(seed):
+    """A library routine: torch CPU float64 autograd through
+    scaled_dot_product_attention with an explicit mask (K/V expanded over the
+    query heads of their group, gradients summed back)."""
+    r = np.random.default_rng(70 + seed)
+    Hkv = int(r.choice([1, 2]))
+    Hq = Hkv * int(r.choice([1, 3]))
+    Lk = int(r.integers(2, 30))
+    Lq = int(r.integers(1, Lk + 1))
+    causal = bool(r.integers(0, 2))
+    window = int(r.choice([-1, 3, 9]))
+    q, k, v = (t.double().numpy() for t in random_dense(2, Hq, Hkv, Lq, Lk, 16, "bf16", 80 + seed))
+    do = r.standard_normal(q.shape)
+    sc = 0.25
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, sc, causal, window)
+    qt = torch.tensor(q.transpose(0, 2, 1, 3), requires_grad=True)
+    kt = torch.tensor(k.transpose(0, 2, 1, 3), requires_grad=True)
+    vt = torch.tensor(v.transpose(0, 2, 1, 3), requires_grad=True)
+    i = torch.arange(Lq)[:, None] + (Lk - Lq)
+    j = torch.arange(Lk)[None, :]
+    m = torch.ones(Lq, Lk, dtype=torch.bool)
+    if causal:
+        m &= j <= i
+    if window >= 0:
+        m &= j >= i - window
+        if not causal:
+            m &= j <= i + window
+    rep = Hq // Hkv
+    o = torch.nn.functional.scaled_dot_product_attention(
+        qt, kt.repeat_interleave(rep, 1), vt.repeat_interleave(rep, 1), attn_mask=m, scale=sc)
+    (o * torch.tensor(do.transpose(0, 2, 1, 3))).sum().backward()
+    np.testing.assert_allclose(dq, qt.grad.numpy().transpose(0, 2, 1, 3), atol=1e-10, rtol=0)
+    np.testing.assert_allclose(dk, kt.grad.numpy().transpose(0, 2, 1, 3), atol=1e-10, rtol=0)
+    np.testing.assert_allclose(dv, vt.grad.numpy().transpose(0, 2, 1, 3), atol=1e-10, rtol=0)
+
+
+def test_p13_backward_sum_identities_and_empty_rows():
+    """Rows of P sum to one, so sum_j dV_j = sum of dO over non-empty rows; the
+    output does not change when every key of a head moves by the same vector
+    (softmax shift invariance, P7), so sum_j dK_j = 0.  Rows with no visible
+    key get dQ = 0 and contribute nothing."""
+    r = np.random.default_rng(90)
+    B, Hq, Hkv, Lq, Lk, D = 2, 4, 2, 9, 6, 5
+    q = r.standard_normal((B, Lq, Hq, D))
+    k = r.standard_normal((B, Lk, Hkv, D))
+    v = r.standard_normal((B, Lk, Hkv, D))
+    do = r.standard_normal((B, Lq, Hq, D))
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, 0.7, causal=True)
+    empty = np.arange(Lq) < Lq - Lk  # causal, bottom-right: the first Lq-Lk rows see nothing
+    assert np.all(dq[:, empty] == 0)
+    for b in range(B):
+        for g in range(Hkv):
+            heads = [h for h in range(Hq) if oracle.kv_head(h, Hq, Hkv) == g]
+            np.testing.assert_allclose(dv[b, :, g].sum(axis=0), do[b][~empty][:, heads].sum(axis=(0, 1)),
+                                       atol=TIGHT)
+            np.testing.assert_allclose(dk[b, :, g].sum(axis=0), 0.0, atol=TIGHT)
+
+
+def test_p13_backward_gqa_is_sum_over_expanded_heads():
+    r = np.random.default_rng(91)
+    B, Hq, Hkv, L, D = 1, 6, 2, 7, 4
+    q = r.standard_normal((B, L, Hq, D))
+    k = r.standard_normal((B, L, Hkv, D))
+    v = r.standard_normal((B, L, Hkv, D))
+    do = r.standard_normal((B, L, Hq, D))
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, 0.3, causal=True)
+    ke, ve = np.repeat(k, Hq // Hkv, axis=2), np.repeat(v, Hq // Hkv, axis=2)
+    dq1, dk1, dv1 = oracle.attention_backward(q, ke, ve, do, 0.3, causal=True)
+    np.testing.assert_allclose(dq, dq1, atol=TIGHT)
+    np.testing.assert_allclose(dk, dk1.reshape(B, L, Hkv, Hq // Hkv, D).sum(axis=3), atol=TIGHT)
+    np.testing.assert_allclose(dv, dv1.reshape(B, L, Hkv, Hq // Hkv, D).sum(axis=3), atol=TIGHT)

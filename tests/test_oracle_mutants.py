@@ -32,6 +32,10 @@ def _pins():
     yield "p12", lambda: [T.test_p12_paged_prefill_equals_dense_and_library(c, w) for c, w in
                           ((True, -1), (True, 3), (False, -1), (False, 2))]
     yield "p12_decode", T.test_p12_paged_prefill_single_token_is_decode
+    yield "p13_fd", lambda: [T.test_p13_backward_matches_finite_differences(c, w) for c, w in
+                             ((False, -1), (True, 1))]
+    yield "p13_torch", lambda: [T.test_p13_backward_matches_torch_autograd(s) for s in range(4)]
+    yield "p13_sums", T.test_p13_backward_sum_identities_and_empty_rows
 
 
 def _failing_pins():
@@ -125,6 +129,34 @@ def _prefill_drops_last_position(q, kc, vc, table, ctx, bs, scale, causal=True, 
     return _orig_prefill(q, kc, vc, table, np.maximum(np.asarray(ctx) - 1, 0), bs, scale, causal, window)
 
 
+def _bwd_variant(jacobian=True, scale_dk=True, sum_heads=True):
+    """A backward with one planted mistake (see the MUTANTS below)."""
+    def bwd(q, k, v, dout, scale, causal=False, window=-1):
+        q, k, v, do = (np.asarray(x, dtype=float) for x in (q, k, v, dout))
+        B, Lq, Hq, D = q.shape
+        Lk, Hkv = k.shape[1], k.shape[2]
+        sc = float(np.float32(scale))
+        ok = OA.allowed_mask(Lq, Lk, causal, window)
+        dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+        for b in range(B):
+            for h in range(Hq):
+                g = h // (Hq // Hkv)
+                P, _ = OA.row_softmax(sc * q[b, :, h] @ k[b, :, g].T, ok)
+                dP = do[b, :, h] @ v[b, :, g].T
+                dS = P * (dP - (P * dP).sum(axis=1, keepdims=True)) if jacobian else P * dP
+                dq[b, :, h] = sc * dS @ k[b, :, g]
+                gk = (sc if scale_dk else 1.0) * dS.T @ q[b, :, h]
+                gv = P.T @ do[b, :, h]
+                if sum_heads:
+                    dk[b, :, g] += gk
+                    dv[b, :, g] += gv
+                else:
+                    dk[b, :, g] = gk
+                    dv[b, :, g] = gv
+        return dq, dk, dv
+    return bwd
+
+
 MUTANTS = {
     "gqa_modulo": ("kv_head", lambda h, Hq, Hkv: h % Hkv),
     "no_scale": ("scores", lambda qr, kr, sc: qr @ kr.T),
@@ -139,6 +171,9 @@ MUTANTS = {
     "gather_ignores_table": ("gather_paged_kv", _gather_ignores_table),
     "prefill_ignores_causal": ("prefill_paged", _prefill_ignores_causal),
     "prefill_drops_last_position": ("prefill_paged", _prefill_drops_last_position),
+    "bwd_no_jacobian_term": ("attention_backward", _bwd_variant(jacobian=False)),
+    "bwd_dk_unscaled": ("attention_backward", _bwd_variant(scale_dk=False)),
+    "bwd_gqa_not_summed": ("attention_backward", _bwd_variant(sum_heads=False)),
 }
 
 
