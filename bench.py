@@ -417,6 +417,36 @@ def main():
             attain = min(PEAK_BF16_TFLOPS, fl / byts * PEAK_HBM_GBS / 1e3)
             detail[name]["frac_attainable"] = round(fl / ms / 1e9 / attain, 4)
             log(f"detail {name}: {detail[name]}")
+        # backward (dq, dk, dv) on the long causal GQA workload and the L=2048
+        # one; algorithmic flops 2.5x the forward's (the recomputed S plus the
+        # dV, dP, dK and dQ products)
+        for name in ("gqa8k_causal", "std2048"):
+            cfg = CONFIGS[name]
+            bq, bk, bv = (t.to(dev) for t in dense_inputs(cfg))
+            bo, bl = ta.attn_fwd(bq, bk, bv, scale=cfg.scale, causal=cfg.causal, window=cfg.window, stream=stream)
+            bdo = torch.randn_like(bo)
+            bdq, bdk, bdv = torch.empty_like(bq), torch.empty_like(bk), torch.empty_like(bv)
+            bws = torch.empty(ta.attn_bwd_workspace_size(cfg.B, cfg.Hq, cfg.Lq), dtype=torch.uint8, device=dev)
+
+            def backward():
+                ta.attn_bwd(bq, bk, bv, bo, bdo, bl, dq=bdq, dk=bdk, dv=bdv, scale=cfg.scale, causal=cfg.causal,
+                            window=cfg.window, workspace=bws, stream=stream)
+
+            for _ in range(2):
+                backward()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(5):
+                backward()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 5
+            fl = 2.5 * causal_flops(cfg.B, cfg.Hq, cfg.Lq, cfg.Lk, cfg.D, cfg.causal)
+            detail["bwd_" + name] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(fl / ms / 1e9, 1),
+                                     "frac_mfma": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
+            log(f"detail bwd_{name}: {detail['bwd_' + name]}")
+            del bq, bk, bv, bo, bl, bdo, bdq, bdk, bdv, bws
+
         # paged prefill: 512 new tokens per sequence over paged contexts
         pcfg = CONFIGS["paged_prefill"]
         pin = prefill_inputs(pcfg)

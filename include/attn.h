@@ -164,6 +164,41 @@ int attn_fwd_paged(const void* q, const void* k_cache, const void* v_cache,
                    float scale, int causal, int window, int dtype, void* stream);
 
 /*
+ * attn_bwd - gradients of attention: dq, dk, dv of L = sum(dout * out) for
+ * the out = attn_fwd(q, k, v, ...) computed with the same arguments.
+ *
+ *   q, out, dout, dq   [B, Lq, Hq,  D]   dtype
+ *   k, v, dk, dv       [B, Lk, Hkv, D]   dtype
+ *   lse                [B, Hq, Lq] fp32, as attn_fwd wrote it (required)
+ *   workspace          >= attn_bwd_workspace_size(B, Hq, Lq) bytes, 16-byte aligned
+ *
+ * The forward keeps only the per-row log-sum-exp, and the backward recomputes
+ * the probability tiles from q and k ("Самовнимание, ядра CUDA и
+ * FlashAttention", section 3, recomputation in the backward pass).  With
+ * P = softmax(scale * q k^T) over the visible keys (same masks as attn_fwd):
+ *   dv = P^T dout;  dS = P * (dout v^T - rowsum(dout * out));
+ *   dq = scale * dS k;  dk = scale * dS^T q.
+ * A K/V head's dk, dv sum over the query heads sharing it (GQA/MQA).  Rows
+ * that see no key (lse = -inf) contribute nothing and get dq = 0.  Results
+ * are rounded once to dtype; no atomics, so repeated calls give the same bits.
+ * The workspace holds two fp32 values per (b, h, row) between the kernels of
+ * one call; calls sharing a workspace must be ordered on one stream.
+ * Empty sizes: B = 0 is a no-op; Lq = 0 writes dk = dv = 0 (no workspace
+ * needed); Lk = 0 writes dq = 0.  Pointers of empty tensors may be NULL.
+ * Errors: ATTN_ERR_NULL, ATTN_ERR_SHAPE, ATTN_ERR_UNSUPPORTED, ATTN_ERR_ALIGN,
+ * ATTN_ERR_WORKSPACE, ATTN_ERR_DEVICE, ATTN_ERR_HIP.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+             void* dq, void* dk, void* dv,
+             int B, int Hq, int Hkv, int Lq, int Lk, int D,
+             float scale, int causal, int window, int dtype,
+             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace attn_bwd needs (a pure host function); 0 when B*Hq*Lq = 0
+ * or the arguments are invalid. */
+size_t attn_bwd_workspace_size(int B, int Hq, int Lq);
+
+/*
  * Bytes of workspace attn_decode_paged needs for these sizes (a pure host
  * function; no device is touched).  Returns 0 when nothing needs a workspace
  * (num_seqs = 0) or when the arguments are invalid.

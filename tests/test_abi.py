@@ -181,3 +181,41 @@ def test_fwd_paged_valid_args_without_gpu_report_device():
     if torch.cuda.is_available():
         pytest.skip("a GPU is present: valid arguments would launch on the fake address")
     assert _fwd_paged() == DEV
+
+
+def _bwd(**kw):
+    a = dict(q=P, k=P, v=P, out=P, dout=P, lse=P, dq=P, dk=P, dv=P, B=1, Hq=4, Hkv=2, Lq=16, Lk=16, D=64,
+             scale=0.125, causal=0, window=-1, dtype=1, ws=P, ws_bytes=1 << 20)
+    a.update(kw)
+    return ta.load_library().attn_bwd(a["q"], a["k"], a["v"], a["out"], a["dout"], a["lse"], a["dq"], a["dk"],
+                                      a["dv"], a["B"], a["Hq"], a["Hkv"], a["Lq"], a["Lk"], a["D"], a["scale"],
+                                      a["causal"], a["window"], a["dtype"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(out=None), NULL), (dict(dout=None), NULL), (dict(lse=None), NULL),
+    (dict(dq=None), NULL), (dict(k=None), NULL), (dict(v=None), NULL), (dict(dk=None), NULL), (dict(dv=None), NULL),
+    (dict(B=-1), SHAPE), (dict(Lq=-1), SHAPE), (dict(Lk=-1), SHAPE), (dict(Hq=0), SHAPE), (dict(Hq=6, Hkv=4), SHAPE),
+    (dict(scale=float("nan")), SHAPE),
+    (dict(D=96), UNSUP), (dict(dtype=5), UNSUP),
+    (dict(q=P_MIS), ALIGN), (dict(dout=P_MIS), ALIGN), (dict(dk=P_MIS), ALIGN), (dict(lse=P + 2), ALIGN),
+    (dict(ws=None), WS), (dict(ws_bytes=16), WS), (dict(ws=P + 4), WS),
+    (dict(B=0, q=None, k=None, v=None, out=None, dout=None, lse=None, dq=None, dk=None, dv=None), OK),
+])
+def test_bwd_validation(kw, code):
+    assert _bwd(**kw) == code
+
+
+def test_bwd_workspace_size():
+    lib = ta.load_library()
+    assert lib.attn_bwd_workspace_size(1, 32, 8192) == 2 * 32 * 8192 * 4
+    assert lib.attn_bwd_workspace_size(2, 3, 5) == 2 * 128  # 30 floats = 120 bytes, each half padded to 16 bytes
+    assert lib.attn_bwd_workspace_size(0, 3, 5) == 0
+    assert lib.attn_bwd_workspace_size(2, 3, -1) == 0
+
+
+def test_bwd_valid_args_without_gpu_report_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: valid arguments would launch on the fake address")
+    assert _bwd() == DEV

@@ -7,6 +7,8 @@ the C ABI declared in include/attn.h, with the same entry-point names:
     attn_fwd(q, k, v, ...)                  q [B,Lq,Hq,D], k/v [B,Lk,Hkv,D]
     attn_decode_paged(q, k_cache, ...)      q [S,Hq,D], caches [N,16,Hkv,D]
     attn_fwd_paged(q, k_cache, ...)         q [B,Lq,Hq,D] over paged caches [N,16,Hkv,D]
+    attn_bwd(q, k, v, out, dout, lse, ...)  gradients dq, dk, dv
+    attn_bwd_workspace_size(B, Hq, Lq)
     attn_decode_paged_workspace_size(...)
     attn_status_string(status)
     attn_hbm_read_probe(buf, sink)          plain streaming read (include/attn_measure.h)
@@ -37,7 +39,7 @@ STATUS = {
     -7: "ATTN_ERR_HIP",
 }
 EXPORTED = ("attn_fwd", "attn_decode_paged", "attn_decode_paged_workspace_size", "attn_status_string",
-            "attn_fwd_paged", "attn_hbm_read_probe")
+            "attn_fwd_paged", "attn_bwd", "attn_bwd_workspace_size", "attn_hbm_read_probe")
 
 _lib = None
 _lock = threading.Lock()
@@ -71,6 +73,11 @@ def load_library() -> ctypes.CDLL:
             lib.attn_fwd_paged.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                            f32, i32, i32, i32, vp]
             lib.attn_fwd_paged.restype = i32
+            lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                     f32, i32, i32, i32, vp, sz, vp]
+            lib.attn_bwd.restype = i32
+            lib.attn_bwd_workspace_size.argtypes = [i32, i32, i32]
+            lib.attn_bwd_workspace_size.restype = sz
             lib.attn_hbm_read_probe.argtypes = [vp, sz, vp, vp]
             lib.attn_hbm_read_probe.restype = i32
             _lib = lib
@@ -276,6 +283,49 @@ def attn_fwd_paged(q, k_cache, v_cache, block_table, ctx_lens, out=None, lse=Non
     if st != 0:
         raise AttnError(st, "attn_fwd_paged")
     return out, lse
+
+
+def attn_bwd_workspace_size(B: int, Hq: int, Lq: int) -> int:
+    return int(load_library().attn_bwd_workspace_size(B, Hq, Lq))
+
+
+def attn_bwd(q, k, v, out, dout, lse, dq=None, dk=None, dv=None, scale: Optional[float] = None,
+             causal: bool = False, window: int = -1, workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of sum(dout * out) for out, lse = attn_fwd(q, k, v, ...)
+    called with the same scale, causal and window."""
+    import torch
+
+    for n, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout), ("lse", lse)):
+        _require_cuda(n, t)
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or out.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("expected q/out/dout [B,Lq,Hq,D] and k, v [B,Lk,Hkv,D]")
+    B, Lq, Hq, D = q.shape
+    Bk, Lk, Hkv, Dk = k.shape
+    if Bk != B or Dk != D or any(t.dtype != q.dtype for t in (k, v, out, dout)):
+        raise ValueError("q, k, v, out, dout disagree in batch, head dim or dtype")
+    if lse.shape != (B, Hq, Lq) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B,Hq,Lq]")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for n, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _require_cuda(n, t)
+        if t.shape != ref.shape or t.dtype != ref.dtype:
+            raise ValueError(f"{n} must match the shape and dtype of its input")
+    need = attn_bwd_workspace_size(B, Hq, Lq)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    st = load_library().attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+                                 lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                 B, Hq, Hkv, Lq, Lk, D, float(scale), int(bool(causal)), int(window),
+                                 _dtype_code(q), ws_ptr, ws_bytes, _stream_handle(stream))
+    if st != 0:
+        raise AttnError(st, "attn_bwd")
+    return dq, dk, dv
 
 
 def attn_hbm_read_probe(buf, sink, stream=None) -> None:

@@ -155,6 +155,53 @@ ATTN_API int attn_fwd_paged(const void* q, const void* k_cache, const void* v_ca
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+ATTN_API size_t attn_bwd_workspace_size(int B, int Hq, int Lq) {
+  if (B <= 0 || Hq <= 0 || Lq <= 0 || !prod_ok(B, Hq, Lq, 8)) return 0;
+  const size_t n = (size_t)B * Hq * Lq;
+  return ((n * 4 + 15) & ~(size_t)15) * 2;  // D, then the base-2 lse, each 16-byte aligned
+}
+
+ATTN_API int attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                      const float* lse, void* dq, void* dk, void* dv,
+                      int B, int Hq, int Hkv, int Lq, int Lk, int D,
+                      float scale, int causal, int window, int dtype,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || Lq < 0 || Lk < 0 || Hq <= 0 || Hkv <= 0) return ATTN_ERR_SHAPE;
+  const bool q_empty = (B == 0 || Lq == 0), kv_empty = (B == 0 || Lk == 0);
+  if (!q_empty && (!q || !out || !dout || !lse || !dq)) return ATTN_ERR_NULL;
+  if (!kv_empty && (!k || !v || !dk || !dv)) return ATTN_ERR_NULL;
+  if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+  if (!std::isfinite(scale)) return ATTN_ERR_SHAPE;
+  if (!supported_d(D) || !supported_dtype(dtype)) return ATTN_ERR_UNSUPPORTED;
+  if (!prod_ok(B, Lq, Hq, D) || !prod_ok(B, Lk, Hkv, D)) return ATTN_ERR_SHAPE;
+  const long long n_qblocks = ((long long)Lq + attn::kPrefillBlockM - 1) / attn::kPrefillBlockM;
+  if (n_qblocks * Hq * (long long)B > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+  if ((((long long)Lk + 127) / 128) * Hkv * (long long)B > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+  for (const void* p : {q, k, v, out, dout, (const void*)dq, (const void*)dk, (const void*)dv})
+    if (!aligned(p, 16)) return ATTN_ERR_ALIGN;
+  if (!aligned(lse, 4)) return ATTN_ERR_ALIGN;
+  if (q_empty && kv_empty) return ATTN_OK;  // nothing to write
+  const size_t need = attn_bwd_workspace_size(B, Hq, Lq);
+  if (need > 0 && (!workspace || !aligned(workspace, 16) || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
+  const int dev = check_device();
+  if (dev != ATTN_OK) return dev;
+
+  attn::BwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = out; a.dout = dout; a.lse = lse;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.Dv = static_cast<float*>(workspace);
+  a.L2 = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) + need / 2) : nullptr;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Lq = Lq; a.Lk = Lk;
+  a.group = Hq / Hkv;
+  a.causal = causal ? 1 : 0;
+  a.window = window < 0 ? -1 : window;
+  a.scale = scale;
+  a.scale_log2 = scale * attn::kLog2e;
+  a.n_qblocks = (int)n_qblocks;
+  hipError_t e = attn::launch_bwd(a, D, dtype, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 // Workspace slots of one decode launch: one per (range, sequence) pair that
 // can leave a partial, indexed range + sequence, so fewer than
 // ranges + sequences; ranges never outnumber the launch's cache blocks.

@@ -1,0 +1,519 @@
+// Attention backward: dQ, dK, dV of L = sum(dO * out) by recomputation.
+//
+// Only the forward's per-row log-sum-exp is kept; every probability tile is
+// recomputed from Q and K ("Самовнимание, ядра CUDA и FlashAttention",
+// section 3: the normalisation statistics are saved and the attention tiles
+// are recomputed on chip in the backward pass).  With S = scale * Q K^T,
+// P = exp(S - lse) (row softmax) and D_i = sum_d dO_id * O_id (which equals
+// sum_j P_ij dP_ij):
+//   dV = P^T dO,   dP = dO V^T,   dS = P * (dP - D),
+//   dK = scale * dS^T Q,   dQ = scale * dS K.
+//
+// Three kernels, no atomics (results are deterministic):
+//   bwd_pre_kernel   D_i per (batch, head, row), and the base-2 lse with +inf
+//                    for rows that see no key (their P is then exactly 0);
+//   bwd_dkdv_kernel  one work-group per (batch, KV head, 128-key block): K and
+//                    V stay in registers, the Q/dO tiles of every query head
+//                    of the group stream through LDS, and dK, dV accumulate in
+//                    registers.  S = Q K^T puts one key in each lane column,
+//                    so P and dS feed dV^T += dO^T P and dK^T += Q^T dS as
+//                    B operands straight from the accumulators; the A operands
+//                    dO^T and Q^T are transposed LDS reads (ds_read_b64_tr_b16)
+//                    that fetch rows in the accumulators' order;
+//   bwd_dq_kernel    one work-group per (batch, head, 128-row block), the
+//                    forward's layout: S^T = K Q^T and dP^T = V dO^T with Q and
+//                    dO in registers, dQ^T += K^T dS^T with K^T read transposed.
+// All MFMAs are v_mfma_f32_32x32x16 on 16-bit operands (P and dS are rounded
+// to the input type), accumulating in fp32.
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+#include "internal.h"
+
+namespace attn {
+
+template <int D>
+struct BwdCfg {
+  static constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  static constexpr int RPI = 1024 / (D * 2);        // rows per 1 KiB direct-to-LDS load
+  static constexpr int DSTEPS = D / 16;             // k-steps over the head dimension
+  static constexpr int DT = D / 32;                 // 32-wide head-dimension tiles
+  static constexpr int BQ = 64;                     // query rows per tile (dK/dV kernel)
+  static constexpr int BK = 128;                    // keys per work-group (dK/dV kernel)
+  static constexpr int BN = 64;                     // keys per tile (dQ kernel)
+  static constexpr int BM = kPrefillBlockM;         // query rows per work-group (dQ kernel)
+  static constexpr int TILE = 64 * D;               // elements of a 64-row tile
+  static constexpr int IPW = 64 / RPI / 4;          // load instructions per wave per 64-row tile
+};
+
+// One swizzle for every backward tile.  Tiles are read both along rows (k
+// over the head dimension: one 16-byte chunk from 32 consecutive rows) and
+// transposed (k over rows); the 8-row period keeps the transposed reads'
+// fixed +8 and +16 row steps on the same chunk pattern.
+__device__ __forceinline__ int bswz(int r) { return r & 7; }
+
+// A buffer resource's byte range, saturated to what the 32-bit field holds.
+__device__ __forceinline__ uint32_t range32(size_t bytes) {
+  return bytes > 0x7fffffffu ? 0x7fffffffu : (uint32_t)bytes;
+}
+
+// ------------------------------------------------------------------ preprocess
+
+template <typename TT, int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
+  using E = typename TT::elem;
+  constexpr int LPR = D / 8;          // lanes per row, 8 elements each
+  constexpr int RPB = 256 / LPR;      // rows per work-group
+  const int tid = threadIdx.x;
+  const long long row = (long long)blockIdx.x * RPB + tid / LPR;  // ((b*Lq + i)*Hq + h)
+  const long long nrows = (long long)a.B * a.Lq * a.Hq;
+  const int c = tid % LPR;
+  float acc = 0.f;
+  if (row < nrows) {
+    using V8 = typename TT::vec8;
+    const V8 o = *(const V8*)((const E*)a.o + row * D + 8 * c);
+    const V8 g = *(const V8*)((const E*)a.dout + row * D + 8 * c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(TT::to_f32(o[e]), TT::to_f32(g[e]), acc);
+  }
+#pragma unroll
+  for (int m = LPR / 2; m > 0; m >>= 1) acc += __shfl_xor(acc, m);
+  if (row < nrows && c == 0) {
+    const long long h = row % a.Hq, bi = row / a.Hq, i = bi % a.Lq, b = bi / a.Lq;
+    const size_t o = ((size_t)b * a.Hq + h) * a.Lq + i;
+    a.Dv[o] = acc;
+    const float l = a.lse[o];
+    a.L2[o] = l == -INFINITY ? INFINITY : l * kLog2e;
+  }
+}
+
+// ------------------------------------------------------------------ dK, dV
+
+template <typename TT, int D>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
+  using C = BwdCfg<D>;
+  using E = typename TT::elem;
+  using V8 = typename TT::vec8;
+  using V4 = typename TT::vec4;
+  __shared__ __attribute__((aligned(16))) E qt0[C::TILE];
+  __shared__ __attribute__((aligned(16))) E qt1[C::TILE];
+  __shared__ __attribute__((aligned(16))) E gt0[C::TILE];   // dO tiles
+  __shared__ __attribute__((aligned(16))) E gt1[C::TILE];
+  __shared__ __attribute__((aligned(16))) float lt0[C::BQ];  // base-2 lse of the tile's rows
+  __shared__ __attribute__((aligned(16))) float lt1[C::BQ];
+  __shared__ __attribute__((aligned(16))) float dt0[C::BQ];  // D of the tile's rows
+  __shared__ __attribute__((aligned(16))) float dt1[C::BQ];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hh = lane >> 5, l32 = lane & 31, j16 = lane & 15, grp = lane >> 4;
+
+  // Key blocks in order (block 0 has the most visible rows when causal).
+  const int n_groups = a.B * a.Hkv;
+  const int kb = blockIdx.x / n_groups, gid = blockIdx.x % n_groups;
+  const int b = gid / a.Hkv, g = gid % a.Hkv;
+  const int k0 = kb * C::BK, kw0 = k0 + wave * 32;
+  const int off = a.Lk - a.Lq;
+  const int W = a.window;
+
+  // Query rows that see at least one key of [k0, k0 + BK) (bottom-right
+  // causal alignment; the window as in the forward).
+  int i_lo = 0, i_hi = a.Lq - 1;
+  const int kl = k0, kh = min(k0 + C::BK, a.Lk) - 1;
+  if (a.causal) i_lo = max(i_lo, kl - off);
+  if (W >= 0) {
+    i_hi = min(i_hi, kh - off + W);
+    if (!a.causal) i_lo = max(i_lo, kl - off - W);
+  }
+  const int qt_lo = i_lo / C::BQ;
+  const int nq = (i_hi >= i_lo) ? i_hi / C::BQ + 1 - qt_lo : 0;
+  const int n_items = nq * a.group;
+
+  // K and V of this lane's key as B operands (k over the head dimension).
+  const size_t kv_rs = (size_t)a.Hkv * D;
+  V8 kreg[C::DSTEPS], vreg[C::DSTEPS];
+  {
+    const uint32_t bytes = kw0 < a.Lk ? range32((((size_t)(a.Lk - kw0) - 1) * kv_rs + D) * sizeof(E)) : 0u;
+    const rsrc_t rk = make_rsrc((const E*)a.k + ((size_t)b * a.Lk + kw0) * kv_rs + (size_t)g * D, bytes);
+    const rsrc_t rv = make_rsrc((const E*)a.v + ((size_t)b * a.Lk + kw0) * kv_rs + (size_t)g * D, bytes);
+#pragma unroll
+    for (int s = 0; s < C::DSTEPS; ++s) {
+      const uint32_t o = (uint32_t)(((size_t)l32 * kv_rs + 16 * s + 8 * hh) * sizeof(E));
+      kreg[s] = __builtin_bit_cast(V8, buf_load16(rk, o));
+      vreg[s] = __builtin_bit_cast(V8, buf_load16(rv, o));
+    }
+  }
+
+  // LDS offsets.  Row read: row l32 of a 32-row block, chunk 2s + hh.
+  int noff[C::DSTEPS];
+#pragma unroll
+  for (int s = 0; s < C::DSTEPS; ++s) noff[s] = l32 * D + (((2 * s + hh) ^ bswz(l32)) << 3);
+  // Transposed read of d-tile dt: rows 4*hh + j16/4 (+16*s, +8), columns
+  // 32*dt + 16*(grp&1) + 4*(j16&3)..+3, so that operand index 8*hh + e is
+  // row 16*s + 8*(e/4) + 4*hh + e%4 -- the accumulators' row order.
+  int toff[C::DT];
+  {
+    const int r = 4 * hh + (j16 >> 2);
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) {
+      const int col = 32 * dt + 16 * (grp & 1) + 4 * (j16 & 3);
+      toff[dt] = r * D + ((((col >> 3) ^ bswz(r)) << 3) + 4 * ((col >> 2) & 1));
+    }
+  }
+
+  // Staging of item it (query head h, 64-row tile qt) into buffer set P.
+  uint32_t src[C::IPW];
+#pragma unroll
+  for (int i = 0; i < C::IPW; ++i) {
+    const int r = (wave * C::IPW + i) * C::RPI + lane / C::CPR;
+    const int p = lane % C::CPR;
+    src[i] = (uint32_t)(((size_t)r * a.Hq * D + ((p ^ bswz(r)) << 3)) * sizeof(E));
+  }
+  auto issue = [&](int it, auto par) {
+    constexpr int P = decltype(par)::value;
+    const int h = g * a.group + it / nq;
+    const int i0 = (qt_lo + it % nq) * C::BQ;
+    const uint32_t bytes = range32((((size_t)(a.Lq - i0) - 1) * a.Hq * D + D) * sizeof(E));
+    const size_t base = (((size_t)b * a.Lq + i0) * a.Hq + h) * D;
+    const rsrc_t rq = make_rsrc((const E*)a.q + base, bytes);
+    const rsrc_t rg = make_rsrc((const E*)a.dout + base, bytes);
+#pragma unroll
+    for (int i = 0; i < C::IPW; ++i) {
+      buf_load16_lds(rq, src[i], (P ? qt1 : qt0) + (wave * C::IPW + i) * C::RPI * D);
+      buf_load16_lds(rg, src[i], (P ? gt1 : gt0) + (wave * C::IPW + i) * C::RPI * D);
+    }
+    {
+      // Every wave loads the 64 rows' statistics (identical bytes), so no
+      // wave-dependent branch sits among the loads.
+      const size_t so = ((size_t)b * a.Hq + h) * a.Lq + i0;
+      const uint32_t sb = (uint32_t)(a.Lq - i0) * 4u;
+      buf_load4_lds(make_rsrc(a.L2 + so, sb), 4u * lane, P ? lt1 : lt0);
+      buf_load4_lds(make_rsrc(a.Dv + so, sb), 4u * lane, P ? dt1 : dt0);
+    }
+  };
+
+  f32x16 dkacc[C::DT], dvacc[C::DT];
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt) {
+    dkacc[dt] = f32x16{};
+    dvacc[dt] = f32x16{};
+  }
+  const float sl2 = a.scale_log2;
+
+  auto body = [&](int it, auto par) {
+    constexpr int P = decltype(par)::value;
+    if (it + 1 < n_items) issue(it + 1, Par<1 - P>{});
+    const E* qs = P ? qt1 : qt0;
+    const E* gs = P ? gt1 : gt0;
+    const float* ls = P ? lt1 : lt0;
+    const float* ds = P ? dt1 : dt0;
+    const int i0 = (qt_lo + it % nq) * C::BQ;
+
+    // Per 32-row block: S = Q K^T and dP = dO V^T (32 rows x 32 keys), then
+    // P = exp2(S * scale * log2(e) - lse2) and dS = P (dP - D), masked, then
+    // dV^T += dO^T P and dK^T += Q^T dS over the block's two row steps of 16.
+    // Register r of the block's accumulators is row 8*(r/4) + 4*hh + r%4.
+    const bool full = (i0 + C::BQ <= a.Lq) && (kw0 + 32 <= a.Lk) && (!a.causal || kw0 + 31 <= i0 + off) &&
+                      (W < 0 || kw0 >= i0 + C::BQ - 1 + off - W) &&
+                      (W < 0 || a.causal || kw0 + 31 <= i0 + off + W);
+    const int key = kw0 + l32;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      f32x16 sacc = f32x16{}, pacc = f32x16{};
+#pragma unroll
+      for (int s = 0; s < C::DSTEPS; ++s) {
+        sacc = TT::mfma32(*(const V8*)(qs + noff[s] + rb * 32 * D), kreg[s], sacc);
+        pacc = TT::mfma32(*(const V8*)(gs + noff[s] + rb * 32 * D), vreg[s], pacc);
+      }
+      f32x4 l4[4], d4[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        l4[q] = *(const f32x4*)(ls + rb * 32 + 8 * q + 4 * hh);
+        d4[q] = *(const f32x4*)(ds + rb * 32 + 8 * q + 4 * hh);
+      }
+      float pv[16], sv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = __builtin_fmaf(sacc[r], sl2, -l4[r >> 2][r & 3]);
+        if (!full) {
+          const int i = i0 + rb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+          const int rel = key - (i + off);
+          const bool vis = i < a.Lq && key < a.Lk && (!a.causal || rel <= 0) && (W < 0 || rel >= -W) &&
+                           (W < 0 || a.causal || rel <= W);
+          x = vis ? x : -INFINITY;
+        }
+        pv[r] = fast_exp2(x);
+        sv[r] = pv[r] * (pacc[r] - d4[r >> 2][r & 3]);
+      }
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {  // row step s = 2*rb + h2: registers 8*h2 .. 8*h2+7
+        const int s = 2 * rb + h2;
+        const V8 bp = __builtin_bit_cast(
+            V8, make_uint4(pack2<TT>(pv[8 * h2], pv[8 * h2 + 1]), pack2<TT>(pv[8 * h2 + 2], pv[8 * h2 + 3]),
+                           pack2<TT>(pv[8 * h2 + 4], pv[8 * h2 + 5]), pack2<TT>(pv[8 * h2 + 6], pv[8 * h2 + 7])));
+        const V8 bs = __builtin_bit_cast(
+            V8, make_uint4(pack2<TT>(sv[8 * h2], sv[8 * h2 + 1]), pack2<TT>(sv[8 * h2 + 2], sv[8 * h2 + 3]),
+                           pack2<TT>(sv[8 * h2 + 4], sv[8 * h2 + 5]), pack2<TT>(sv[8 * h2 + 6], sv[8 * h2 + 7])));
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) {
+          const E* g0 = gs + toff[dt] + 16 * s * D;
+          const E* q0p = qs + toff[dt] + 16 * s * D;
+          dvacc[dt] = TT::mfma32(cat4<V4, V8>(TT::read_tr(g0), TT::read_tr(g0 + 8 * D)), bp, dvacc[dt]);
+          dkacc[dt] = TT::mfma32(cat4<V4, V8>(TT::read_tr(q0p), TT::read_tr(q0p + 8 * D)), bs, dkacc[dt]);
+        }
+      }
+    }
+    wait_vmem();
+    __syncthreads();
+  };
+
+  if (n_items > 0) {
+    issue(0, Par<0>{});
+    wait_vmem();
+    __syncthreads();
+    for (int it = 0; it < n_items; it += 2) {
+      body(it, Par<0>{});
+      if (it + 1 < n_items) body(it + 1, Par<1>{});
+    }
+  }
+
+  // dK = scale * (dK^T)^T, dV: register r of d-tile dt is head-dim element
+  // 32*dt + 8*(r/4) + 4*hh + r%4 of this lane's key.
+  if (kw0 + l32 < a.Lk) {
+    const size_t ro = (((size_t)b * a.Lk + kw0 + l32) * a.Hkv + g) * D;
+    E* dkr = (E*)a.dk + ro;
+    E* dvr = (E*)a.dv + ro;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float sc = a.scale;
+        *(uint2*)(dkr + 32 * dt + 8 * q4 + 4 * hh) =
+            make_uint2(pack2<TT>(dkacc[dt][4 * q4] * sc, dkacc[dt][4 * q4 + 1] * sc),
+                       pack2<TT>(dkacc[dt][4 * q4 + 2] * sc, dkacc[dt][4 * q4 + 3] * sc));
+        *(uint2*)(dvr + 32 * dt + 8 * q4 + 4 * hh) =
+            make_uint2(pack2<TT>(dvacc[dt][4 * q4], dvacc[dt][4 * q4 + 1]),
+                       pack2<TT>(dvacc[dt][4 * q4 + 2], dvacc[dt][4 * q4 + 3]));
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ dQ
+
+template <typename TT, int D>
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
+  using C = BwdCfg<D>;
+  using E = typename TT::elem;
+  using V8 = typename TT::vec8;
+  using V4 = typename TT::vec4;
+  __shared__ __attribute__((aligned(16))) E kt0[C::TILE];
+  __shared__ __attribute__((aligned(16))) E kt1[C::TILE];
+  __shared__ __attribute__((aligned(16))) E vt0[C::TILE];
+  __shared__ __attribute__((aligned(16))) E vt1[C::TILE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hh = lane >> 5, l32 = lane & 31, j16 = lane & 15, grp = lane >> 4;
+
+  const int n_heads = a.B * a.Hq;
+  const int qb_rank = blockIdx.x / n_heads, bh = blockIdx.x % n_heads;
+  const int b = bh / a.Hq, hq = bh % a.Hq, g = hq / a.group;
+  const int qb = a.causal ? (a.n_qblocks - 1 - qb_rank) : qb_rank;  // heaviest first when causal
+  const int q0 = qb * C::BM;
+  const int off = a.Lk - a.Lq;
+  const int W = a.window;
+
+  // Key tiles of the work-group and the keys this lane's row sees.
+  const int row_hi = min(q0 + C::BM, a.Lq) - 1;
+  int j_lo = 0, j_hi = a.Lk - 1;
+  if (a.causal) j_hi = min(j_hi, row_hi + off);
+  if (W >= 0) {
+    j_lo = max(j_lo, q0 + off - W);
+    if (!a.causal) j_hi = min(j_hi, row_hi + off + W);
+  }
+  const int t_lo = j_lo / C::BN;
+  const int t_hi = (j_hi >= j_lo) ? j_hi / C::BN + 1 : t_lo;
+  const int qi = q0 + wave * 32 + l32;
+  int jlo_row = 0, jhi_row = a.Lk - 1;
+  if (a.causal) jhi_row = min(jhi_row, qi + off);
+  if (W >= 0) {
+    jlo_row = max(jlo_row, qi + off - W);
+    if (!a.causal) jhi_row = min(jhi_row, qi + off + W);
+  }
+  if (qi >= a.Lq) jhi_row = jlo_row - 1;  // rows past Lq see nothing
+  const int wr_lo = q0 + wave * 32, wr_hi = min(wr_lo + 31, a.Lq - 1);
+
+  // Q and dO of this lane's row as B operands; the row's statistics.
+  V8 qf[C::DSTEPS], gf[C::DSTEPS];
+  float l2 = INFINITY, dvv = 0.f;
+  {
+    const size_t base = (((size_t)b * a.Lq + q0) * a.Hq + hq) * D;
+    const uint32_t bytes = range32((((size_t)(a.Lq - q0) - 1) * a.Hq * D + D) * sizeof(E));
+    const rsrc_t rq = make_rsrc((const E*)a.q + base, bytes);
+    const rsrc_t rg = make_rsrc((const E*)a.dout + base, bytes);
+    const uint32_t o = (uint32_t)(((size_t)(wave * 32 + l32) * a.Hq * D + 8 * hh) * sizeof(E));
+#pragma unroll
+    for (int s = 0; s < C::DSTEPS; ++s) {
+      qf[s] = __builtin_bit_cast(V8, buf_load16(rq, o + 32 * s));
+      gf[s] = __builtin_bit_cast(V8, buf_load16(rg, o + 32 * s));
+    }
+    if (qi < a.Lq) {
+      const size_t so = ((size_t)b * a.Hq + hq) * a.Lq + qi;
+      l2 = a.L2[so];
+      dvv = a.Dv[so];
+    }
+  }
+
+  int noff[C::DSTEPS];
+#pragma unroll
+  for (int s = 0; s < C::DSTEPS; ++s) noff[s] = l32 * D + (((2 * s + hh) ^ bswz(l32)) << 3);
+  int toff[C::DT];
+  {
+    const int r = 4 * hh + (j16 >> 2);
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) {
+      const int col = 32 * dt + 16 * (grp & 1) + 4 * (j16 & 3);
+      toff[dt] = r * D + ((((col >> 3) ^ bswz(r)) << 3) + 4 * ((col >> 2) & 1));
+    }
+  }
+
+  const size_t kv_rs = (size_t)a.Hkv * D;
+  const E* kb = (const E*)a.k + ((size_t)b * a.Lk * a.Hkv + g) * D;
+  const E* vb = (const E*)a.v + ((size_t)b * a.Lk * a.Hkv + g) * D;
+  uint32_t src[C::IPW];
+#pragma unroll
+  for (int i = 0; i < C::IPW; ++i) {
+    const int r = (wave * C::IPW + i) * C::RPI + lane / C::CPR;
+    const int p = lane % C::CPR;
+    src[i] = (uint32_t)(((size_t)r * kv_rs + ((p ^ bswz(r)) << 3)) * sizeof(E));
+  }
+  auto issue = [&](int t, auto par) {
+    constexpr int P = decltype(par)::value;
+    const uint32_t bytes = t < t_hi ? range32((((size_t)(a.Lk - t * C::BN) - 1) * kv_rs + D) * sizeof(E)) : 0u;
+    const rsrc_t rk = make_rsrc(kb + (size_t)t * C::BN * kv_rs, bytes);
+    const rsrc_t rv = make_rsrc(vb + (size_t)t * C::BN * kv_rs, bytes);
+#pragma unroll
+    for (int i = 0; i < C::IPW; ++i) {
+      buf_load16_lds(rk, src[i], (P ? kt1 : kt0) + (wave * C::IPW + i) * C::RPI * D);
+      buf_load16_lds(rv, src[i], (P ? vt1 : vt0) + (wave * C::IPW + i) * C::RPI * D);
+    }
+  };
+
+  f32x16 dqacc[C::DT];
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt) dqacc[dt] = f32x16{};
+  const float sl2 = a.scale_log2;
+
+  auto body = [&](int t, auto par) {
+    constexpr int P = decltype(par)::value;
+    if (t + 1 < t_hi) issue(t + 1, Par<1 - P>{});
+    const E* ks = P ? kt1 : kt0;
+    const E* vs = P ? vt1 : vt0;
+    // S^T = K Q^T and dP^T = V dO^T: 64 keys (two halves) x 32 rows.
+    f32x16 st[2], pt[2];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      st[kh] = f32x16{};
+      pt[kh] = f32x16{};
+    }
+#pragma unroll
+    for (int s = 0; s < C::DSTEPS; ++s) {
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        st[kh] = TT::mfma32(*(const V8*)(ks + noff[s] + kh * 32 * D), qf[s], st[kh]);
+        pt[kh] = TT::mfma32(*(const V8*)(vs + noff[s] + kh * 32 * D), gf[s], pt[kh]);
+      }
+    }
+    // Register r of half kh is key t*BN + kh*32 + 8*(r/4) + 4*hh + r%4.
+    const int jt = t * C::BN;
+    const bool full = (jt + C::BN <= a.Lk) && (!a.causal || jt + C::BN - 1 <= wr_lo + off) &&
+                      (W < 0 || jt >= wr_hi + off - W) && (W < 0 || a.causal || jt + C::BN - 1 <= wr_lo + off + W) &&
+                      (wr_lo + 31 < a.Lq);
+    uint32_t pw[4][4];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      float sv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = __builtin_fmaf(st[kh][r], sl2, -l2);
+        if (!full) {
+          const int j = jt + kh * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+          x = (j >= jlo_row && j <= jhi_row) ? x : -INFINITY;
+        }
+        const float p = fast_exp2(x);
+        sv[r] = p * (pt[kh][r] - dvv);
+      }
+#pragma unroll
+      for (int m = 0; m < 8; ++m) pw[2 * kh + (m >> 2)][m & 3] = pack2<TT>(sv[2 * m], sv[2 * m + 1]);
+    }
+    // dQ^T += K^T dS^T over the 4 key steps of 16.
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const V8 bs = __builtin_bit_cast(V8, make_uint4(pw[s][0], pw[s][1], pw[s][2], pw[s][3]));
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) {
+        const E* k0p = ks + toff[dt] + 16 * s * D;
+        dqacc[dt] = TT::mfma32(cat4<V4, V8>(TT::read_tr(k0p), TT::read_tr(k0p + 8 * D)), bs, dqacc[dt]);
+      }
+    }
+    wait_vmem();
+    __syncthreads();
+  };
+
+  if (t_lo < t_hi) {
+    issue(t_lo, Par<0>{});
+    wait_vmem();
+    __syncthreads();
+    for (int t = t_lo; t < t_hi; t += 2) {
+      body(t, Par<0>{});
+      if (t + 1 < t_hi) body(t + 1, Par<1>{});
+    }
+  }
+
+  if (qi < a.Lq) {
+    E* row = (E*)a.dq + (((size_t)b * a.Lq + qi) * a.Hq + hq) * D;
+    const float sc = a.scale;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        *(uint2*)(row + 32 * dt + 8 * q4 + 4 * hh) =
+            make_uint2(pack2<TT>(dqacc[dt][4 * q4] * sc, dqacc[dt][4 * q4 + 1] * sc),
+                       pack2<TT>(dqacc[dt][4 * q4 + 2] * sc, dqacc[dt][4 * q4 + 3] * sc));
+      }
+    }
+  }
+}
+
+template <typename TT, int D>
+static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
+  using C = BwdCfg<D>;
+  const long long rows = (long long)a.B * a.Lq * a.Hq;
+  hipError_t e = hipSuccess;
+  if (rows > 0) {
+    const long long pre_blocks = (rows + 256 / (D / 8) - 1) / (256 / (D / 8));
+    hipLaunchKernelGGL((bwd_pre_kernel<TT, D>), dim3((unsigned)pre_blocks), dim3(256), 0, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.Lk > 0) {
+    const long long kblocks = (long long)((a.Lk + C::BK - 1) / C::BK) * a.B * a.Hkv;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<TT, D>), dim3((unsigned)kblocks), dim3(256), 0, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const long long qblocks = (long long)a.n_qblocks * a.B * a.Hq;
+  if (qblocks > 0) {
+    hipLaunchKernelGGL((bwd_dq_kernel<TT, D>), dim3((unsigned)qblocks), dim3(256), 0, stream, a);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+hipError_t launch_bwd(const BwdArgs& a, int D, int dtype, hipStream_t stream) {
+  if (dtype == 1) return D == 128 ? launch_bwd_t<BF16, 128>(a, stream) : launch_bwd_t<BF16, 64>(a, stream);
+  return D == 128 ? launch_bwd_t<F16, 128>(a, stream) : launch_bwd_t<F16, 64>(a, stream);
+}
+
+}  // namespace attn

@@ -198,8 +198,33 @@ __device__ __forceinline__ void buf_load16_lds(rsrc_t r, uint32_t byte_off, void
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_dst, 16, byte_off, 0,
                                            0, 0);
 }
+// The 4-byte form: lane i's dword lands at lds_dst + 4*i.
+__device__ __forceinline__ void buf_load4_lds(rsrc_t r, uint32_t byte_off, void* lds_dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_dst, 4, byte_off, 0,
+                                           0, 0);
+}
 // s_waitcnt vmcnt(0): every vector-memory load of this wave has landed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Compile-time buffer parity of a double-buffered loop body.
+template <int P>
+struct Par {
+  static constexpr int value = P;
+};
+
+// Two fp32 values rounded (to nearest even) to the element type and packed.
+template <typename TT>
+__device__ __forceinline__ uint32_t pack2(float a, float b);
+template <>
+__device__ __forceinline__ uint32_t pack2<BF16>(float a, float b) {
+  typedef __bf16 v2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, (v2){(__bf16)a, (__bf16)b});
+}
+template <>
+__device__ __forceinline__ uint32_t pack2<F16>(float a, float b) {
+  typedef _Float16 v2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, (v2){(_Float16)a, (_Float16)b});
+}
 
 template <typename V4, typename V8>
 __device__ __forceinline__ V8 cat4(V4 lo, V4 hi) {

@@ -87,23 +87,6 @@ __device__ __forceinline__ int v_swz(int r) {
 // rescale of the output accumulator is skipped on almost every tile.
 constexpr float kRescaleThreshold = 8.0f;
 
-template <typename TT>
-__device__ __forceinline__ uint32_t pack2(float a, float b);
-template <>
-__device__ __forceinline__ uint32_t pack2<BF16>(float a, float b) {
-  typedef __bf16 v2 __attribute__((ext_vector_type(2)));
-  return __builtin_bit_cast(uint32_t, (v2){(__bf16)a, (__bf16)b});
-}
-template <>
-__device__ __forceinline__ uint32_t pack2<F16>(float a, float b) {
-  typedef _Float16 v2 __attribute__((ext_vector_type(2)));
-  return __builtin_bit_cast(uint32_t, (v2){(_Float16)a, (_Float16)b});
-}
-
-template <int P>
-struct Par {
-  static constexpr int value = P;
-};
 
 template <typename TT, int D, bool PAGED>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {

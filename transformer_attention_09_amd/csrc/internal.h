@@ -50,6 +50,29 @@ struct DecArgs {
   float scale_log2;
 };
 
+// Backward.  dout, out and lse come from the forward; Dv and L2 are the
+// workspace rows written by the preprocess kernel ([B, Hq, Lq] fp32 each).
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* Dv;  // sum_d dO * O per row
+  float* L2;  // lse * log2(e), +inf for rows that see no key
+  int B, Hq, Hkv, Lq, Lk;
+  int group;
+  int causal;
+  int window;
+  float scale;
+  float scale_log2;
+  int n_qblocks;
+};
+
 constexpr int kPrefillBlockM = 128;
 constexpr int kPagedBlock = 16;  // tokens per cache block (both paged entry points)
 constexpr float kLog2e = 1.44269504088896340736f;
@@ -62,6 +85,7 @@ constexpr int kDecodeWavesPerCU = 4;
 
 hipError_t launch_fwd(const FwdArgs& a, int D, int dtype, hipStream_t stream);
 hipError_t launch_fwd_paged(const FwdArgs& a, int D, int dtype, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& a, int D, int dtype, hipStream_t stream);
 hipError_t launch_decode(const DecArgs& a, int D, int dtype, hipStream_t stream);
 hipError_t launch_hbm_read(const void* p, size_t bytes, unsigned* sink, int cus, hipStream_t stream);
 
