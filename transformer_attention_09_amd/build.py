@@ -25,6 +25,10 @@ HIPCC_FLAGS = [
     "-fvisibility=hidden",
     # Keep the compiler from forming packed fp32 (v_pk_*_f32) arithmetic.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the vector ALU reads them directly
+    # (scores, rescales, epilogues), where accumulators in AccVGPRs would need
+    # a v_accvgpr copy for every such use.
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wno-unused-command-line-argument",
 ]
 

@@ -12,10 +12,13 @@
 // Three kernels, no atomics (results are deterministic):
 //   bwd_pre_kernel   D_i per (batch, head, row), and the base-2 lse with +inf
 //                    for rows that see no key (their P is then exactly 0);
-//   bwd_dkdv_kernel  one work-group per (batch, KV head, 128-key block): K and
-//                    V stay in registers, the Q/dO tiles of every query head
-//                    of the group stream through LDS, and dK, dV accumulate in
-//                    registers.  S = Q K^T puts one key in each lane column,
+//   bwd_dkdv_kernel  one work-group per (batch, KV head, 128-key block), 8 waves:
+//                    wave w takes keys 32*(w%4).. and row half w/4 of every
+//                    64-row tile, so each SIMD runs two waves.  The block's K
+//                    and V sit in LDS, the Q/dO tiles of every query head of
+//                    the group stream through LDS, dK and dV accumulate in
+//                    registers, and the two row halves' sums meet in LDS once
+//                    at the end.  S = Q K^T puts one key in each lane column,
 //                    so P and dS feed dV^T += dO^T P and dK^T += Q^T dS as
 //                    B operands straight from the accumulators; the A operands
 //                    dO^T and Q^T are transposed LDS reads (ds_read_b64_tr_b16)
@@ -90,7 +93,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 // ------------------------------------------------------------------ dK, dV
 
 template <typename TT, int D>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   using C = BwdCfg<D>;
   using E = typename TT::elem;
   using V8 = typename TT::vec8;
@@ -103,16 +106,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float lt1[C::BQ];
   __shared__ __attribute__((aligned(16))) float dt0[C::BQ];  // D of the tile's rows
   __shared__ __attribute__((aligned(16))) float dt1[C::BQ];
+  __shared__ __attribute__((aligned(16))) E kblk[C::BK * D];  // the work-group's K and V rows
+  __shared__ __attribute__((aligned(16))) E vblk[C::BK * D];
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7
+  const int ks = wave & 3, rh = wave >> 2;                      // key slice, row half
   const int hh = lane >> 5, l32 = lane & 31, j16 = lane & 15, grp = lane >> 4;
 
   // Key blocks in order (block 0 has the most visible rows when causal).
   const int n_groups = a.B * a.Hkv;
   const int kb = blockIdx.x / n_groups, gid = blockIdx.x % n_groups;
   const int b = gid / a.Hkv, g = gid % a.Hkv;
-  const int k0 = kb * C::BK, kw0 = k0 + wave * 32;
+  const int k0 = kb * C::BK, kw0 = k0 + ks * 32;
   const int off = a.Lk - a.Lq;
   const int W = a.window;
 
@@ -129,18 +135,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int nq = (i_hi >= i_lo) ? i_hi / C::BQ + 1 - qt_lo : 0;
   const int n_items = nq * a.group;
 
-  // K and V of this lane's key as B operands (k over the head dimension).
+  // K and V of the block's keys go to LDS once (rows past Lk load as zeros);
+  // each wave reads its 32 keys' rows as B operands (k over the head dim).
   const size_t kv_rs = (size_t)a.Hkv * D;
-  V8 kreg[C::DSTEPS], vreg[C::DSTEPS];
   {
-    const uint32_t bytes = kw0 < a.Lk ? range32((((size_t)(a.Lk - kw0) - 1) * kv_rs + D) * sizeof(E)) : 0u;
-    const rsrc_t rk = make_rsrc((const E*)a.k + ((size_t)b * a.Lk + kw0) * kv_rs + (size_t)g * D, bytes);
-    const rsrc_t rv = make_rsrc((const E*)a.v + ((size_t)b * a.Lk + kw0) * kv_rs + (size_t)g * D, bytes);
+    const uint32_t bytes = k0 < a.Lk ? range32((((size_t)(a.Lk - k0) - 1) * kv_rs + D) * sizeof(E)) : 0u;
+    const rsrc_t rk = make_rsrc((const E*)a.k + ((size_t)b * a.Lk + k0) * kv_rs + (size_t)g * D, bytes);
+    const rsrc_t rv = make_rsrc((const E*)a.v + ((size_t)b * a.Lk + k0) * kv_rs + (size_t)g * D, bytes);
+    constexpr int IPB = C::BK / C::RPI / 8;  // load instructions per wave for 128 rows
 #pragma unroll
-    for (int s = 0; s < C::DSTEPS; ++s) {
-      const uint32_t o = (uint32_t)(((size_t)l32 * kv_rs + 16 * s + 8 * hh) * sizeof(E));
-      kreg[s] = __builtin_bit_cast(V8, buf_load16(rk, o));
-      vreg[s] = __builtin_bit_cast(V8, buf_load16(rv, o));
+    for (int i = 0; i < IPB; ++i) {
+      const int r = (wave * IPB + i) * C::RPI + lane / C::CPR;
+      const int p = lane % C::CPR;
+      const uint32_t o = (uint32_t)(((size_t)r * kv_rs + ((p ^ bswz(r)) << 3)) * sizeof(E));
+      buf_load16_lds(rk, o, kblk + (wave * IPB + i) * C::RPI * D);
+      buf_load16_lds(rv, o, vblk + (wave * IPB + i) * C::RPI * D);
     }
   }
 
@@ -148,6 +157,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   int noff[C::DSTEPS];
 #pragma unroll
   for (int s = 0; s < C::DSTEPS; ++s) noff[s] = l32 * D + (((2 * s + hh) ^ bswz(l32)) << 3);
+  const int koff = ks * 32 * D;  // the wave's 32 keys inside the K/V block
   // Transposed read of d-tile dt: rows 4*hh + j16/4 (+16*s, +8), columns
   // 32*dt + 16*(grp&1) + 4*(j16&3)..+3, so that operand index 8*hh + e is
   // row 16*s + 8*(e/4) + 4*hh + e%4 -- the accumulators' row order.
@@ -162,10 +172,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   }
 
   // Staging of item it (query head h, 64-row tile qt) into buffer set P.
-  uint32_t src[C::IPW];
+  constexpr int IPT8 = C::BQ / C::RPI / 8;  // load instructions per wave per tile
+  uint32_t src[IPT8];
 #pragma unroll
-  for (int i = 0; i < C::IPW; ++i) {
-    const int r = (wave * C::IPW + i) * C::RPI + lane / C::CPR;
+  for (int i = 0; i < IPT8; ++i) {
+    const int r = (wave * IPT8 + i) * C::RPI + lane / C::CPR;
     const int p = lane % C::CPR;
     src[i] = (uint32_t)(((size_t)r * a.Hq * D + ((p ^ bswz(r)) << 3)) * sizeof(E));
   }
@@ -178,9 +189,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     const rsrc_t rq = make_rsrc((const E*)a.q + base, bytes);
     const rsrc_t rg = make_rsrc((const E*)a.dout + base, bytes);
 #pragma unroll
-    for (int i = 0; i < C::IPW; ++i) {
-      buf_load16_lds(rq, src[i], (P ? qt1 : qt0) + (wave * C::IPW + i) * C::RPI * D);
-      buf_load16_lds(rg, src[i], (P ? gt1 : gt0) + (wave * C::IPW + i) * C::RPI * D);
+    for (int i = 0; i < IPT8; ++i) {
+      buf_load16_lds(rq, src[i], (P ? qt1 : qt0) + (wave * IPT8 + i) * C::RPI * D);
+      buf_load16_lds(rg, src[i], (P ? gt1 : gt0) + (wave * IPT8 + i) * C::RPI * D);
     }
     {
       // Every wave loads the 64 rows' statistics (identical bytes), so no
@@ -209,51 +220,59 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     const float* ds = P ? dt1 : dt0;
     const int i0 = (qt_lo + it % nq) * C::BQ;
 
-    // Per 32-row block: S = Q K^T and dP = dO V^T (32 rows x 32 keys), then
-    // P = exp2(S * scale * log2(e) - lse2) and dS = P (dP - D), masked, then
-    // dV^T += dO^T P and dK^T += Q^T dS over the block's two row steps of 16.
-    // Register r of the block's accumulators is row 8*(r/4) + 4*hh + r%4.
-    const bool full = (i0 + C::BQ <= a.Lq) && (kw0 + 32 <= a.Lk) && (!a.causal || kw0 + 31 <= i0 + off) &&
-                      (W < 0 || kw0 >= i0 + C::BQ - 1 + off - W) &&
-                      (W < 0 || a.causal || kw0 + 31 <= i0 + off + W);
+    // This wave's 32-row block rb = rh: S = Q K^T and dP = dO V^T (32 rows x
+    // 32 keys), then P = exp2(S * scale * log2(e) - lse2) and dS = P (dP - D),
+    // masked, then dV^T += dO^T P and dK^T += Q^T dS over its two row steps
+    // of 16.  Register r of the accumulators is row 8*(r/4) + 4*hh + r%4.
+    const int r0 = i0 + 32 * rh;
+    const bool full = (r0 + 32 <= a.Lq) && (kw0 + 32 <= a.Lk) && (!a.causal || kw0 + 31 <= r0 + off) &&
+                      (W < 0 || kw0 >= r0 + 31 + off - W) && (W < 0 || a.causal || kw0 + 31 <= r0 + off + W);
     const int key = kw0 + l32;
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    {
+      const int rb = rh;
       f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
       for (int s = 0; s < C::DSTEPS; ++s) {
-        sacc = TT::mfma32(*(const V8*)(qs + noff[s] + rb * 32 * D), kreg[s], sacc);
-        pacc = TT::mfma32(*(const V8*)(gs + noff[s] + rb * 32 * D), vreg[s], pacc);
+        sacc = TT::mfma32(*(const V8*)(qs + noff[s] + rb * 32 * D), *(const V8*)(kblk + koff + noff[s]), sacc);
+        pacc = TT::mfma32(*(const V8*)(gs + noff[s] + rb * 32 * D), *(const V8*)(vblk + koff + noff[s]), pacc);
       }
-      f32x4 l4[4], d4[4];
+      // Two row steps of 16 (registers 8*h2 .. 8*h2+7): their P and dS, packed
+      // to the input type, then the step's dV and dK products.
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        l4[q] = *(const f32x4*)(ls + rb * 32 + 8 * q + 4 * hh);
-        d4[q] = *(const f32x4*)(ds + rb * 32 + 8 * q + 4 * hh);
-      }
-      float pv[16], sv[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = __builtin_fmaf(sacc[r], sl2, -l4[r >> 2][r & 3]);
-        if (!full) {
-          const int i = i0 + rb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-          const int rel = key - (i + off);
-          const bool vis = i < a.Lq && key < a.Lk && (!a.causal || rel <= 0) && (W < 0 || rel >= -W) &&
-                           (W < 0 || a.causal || rel <= W);
-          x = vis ? x : -INFINITY;
-        }
-        pv[r] = fast_exp2(x);
-        sv[r] = pv[r] * (pacc[r] - d4[r >> 2][r & 3]);
-      }
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {  // row step s = 2*rb + h2: registers 8*h2 .. 8*h2+7
+      for (int h2 = 0; h2 < 2; ++h2) {
         const int s = 2 * rb + h2;
-        const V8 bp = __builtin_bit_cast(
-            V8, make_uint4(pack2<TT>(pv[8 * h2], pv[8 * h2 + 1]), pack2<TT>(pv[8 * h2 + 2], pv[8 * h2 + 3]),
-                           pack2<TT>(pv[8 * h2 + 4], pv[8 * h2 + 5]), pack2<TT>(pv[8 * h2 + 6], pv[8 * h2 + 7])));
-        const V8 bs = __builtin_bit_cast(
-            V8, make_uint4(pack2<TT>(sv[8 * h2], sv[8 * h2 + 1]), pack2<TT>(sv[8 * h2 + 2], sv[8 * h2 + 3]),
-                           pack2<TT>(sv[8 * h2 + 4], sv[8 * h2 + 5]), pack2<TT>(sv[8 * h2 + 6], sv[8 * h2 + 7])));
+        float pv[8], sv[8];
+        const f32x4 lA = *(const f32x4*)(ls + rb * 32 + 16 * h2 + 4 * hh);
+        const f32x4 lB = *(const f32x4*)(ls + rb * 32 + 16 * h2 + 8 + 4 * hh);
+        const f32x4 dA = *(const f32x4*)(ds + rb * 32 + 16 * h2 + 4 * hh);
+        const f32x4 dB = *(const f32x4*)(ds + rb * 32 + 16 * h2 + 8 + 4 * hh);
+        if (full) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int r = 8 * h2 + e;
+            const float lv = e < 4 ? lA[e] : lB[e - 4], dv = e < 4 ? dA[e] : dB[e - 4];
+            pv[e] = fast_exp2(__builtin_fmaf(sacc[r], sl2, -lv));
+            sv[e] = pv[e] * (pacc[r] - dv);
+          }
+        } else {
+          asm volatile("" ::: "memory");  // a real branch: edge tiles are rare
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int r = 8 * h2 + e;
+            const float lv = e < 4 ? lA[e] : lB[e - 4], dv = e < 4 ? dA[e] : dB[e - 4];
+            const int i = i0 + rb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+            const int rel = key - (i + off);
+            const bool vis = (i < a.Lq) & (key < a.Lk) & (!a.causal | (rel <= 0)) & ((W < 0) | (rel >= -W)) &
+                             ((W < 0) | a.causal | (rel <= W));
+            const float x = __builtin_fmaf(sacc[r], sl2, -lv);
+            pv[e] = fast_exp2(vis ? x : -INFINITY);
+            sv[e] = pv[e] * (pacc[r] - dv);
+          }
+        }
+        const V8 bp = __builtin_bit_cast(V8, make_uint4(pack2<TT>(pv[0], pv[1]), pack2<TT>(pv[2], pv[3]),
+                                                        pack2<TT>(pv[4], pv[5]), pack2<TT>(pv[6], pv[7])));
+        const V8 bs = __builtin_bit_cast(V8, make_uint4(pack2<TT>(sv[0], sv[1]), pack2<TT>(sv[2], sv[3]),
+                                                        pack2<TT>(sv[4], sv[5]), pack2<TT>(sv[6], sv[7])));
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
           const E* g0 = gs + toff[dt] + 16 * s * D;
@@ -277,23 +296,48 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     }
   }
 
-  // dK = scale * (dK^T)^T, dV: register r of d-tile dt is head-dim element
+  // The two row halves' sums meet in LDS: row half 1 parks its dK^T, dV^T
+  // (each lane its own 16-byte slots) in the freed tile and K/V buffers, row
+  // half 0 adds them and stores.  Register r of d-tile dt is head-dim element
   // 32*dt + 8*(r/4) + 4*hh + r%4 of this lane's key.
-  if (kw0 + l32 < a.Lk) {
-    const size_t ro = (((size_t)b * a.Lk + kw0 + l32) * a.Hkv + g) * D;
-    E* dkr = (E*)a.dk + ro;
-    E* dvr = (E*)a.dv + ro;
+  wait_vmem();
+  __syncthreads();
+  {
+    static_assert(C::DT * 16 * 64 * 4 <= C::TILE * (int)sizeof(E), "a slice's partial sums fit a tile buffer");
+    float* pk = (float*)(ks == 0 ? qt0 : ks == 1 ? qt1 : ks == 2 ? gt0 : gt1);
+    float* pv = (float*)((ks < 2 ? kblk : vblk) + (ks & 1) * (C::BK / 2) * D);
+    if (rh == 1) {
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) {
+      for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const float sc = a.scale;
-        *(uint2*)(dkr + 32 * dt + 8 * q4 + 4 * hh) =
-            make_uint2(pack2<TT>(dkacc[dt][4 * q4] * sc, dkacc[dt][4 * q4 + 1] * sc),
-                       pack2<TT>(dkacc[dt][4 * q4 + 2] * sc, dkacc[dt][4 * q4 + 3] * sc));
-        *(uint2*)(dvr + 32 * dt + 8 * q4 + 4 * hh) =
-            make_uint2(pack2<TT>(dvacc[dt][4 * q4], dvacc[dt][4 * q4 + 1]),
-                       pack2<TT>(dvacc[dt][4 * q4 + 2], dvacc[dt][4 * q4 + 3]));
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int j = dt * 4 + q4;
+          *(f32x4*)(pk + (j * 64 + lane) * 4) = f32x4{dkacc[dt][4 * q4], dkacc[dt][4 * q4 + 1],
+                                                       dkacc[dt][4 * q4 + 2], dkacc[dt][4 * q4 + 3]};
+          *(f32x4*)(pv + (j * 64 + lane) * 4) = f32x4{dvacc[dt][4 * q4], dvacc[dt][4 * q4 + 1],
+                                                       dvacc[dt][4 * q4 + 2], dvacc[dt][4 * q4 + 3]};
+        }
+    }
+    __syncthreads();
+    if (rh == 0 && kw0 + l32 < a.Lk) {
+      const size_t ro = (((size_t)b * a.Lk + kw0 + l32) * a.Hkv + g) * D;
+      E* dkr = (E*)a.dk + ro;
+      E* dvr = (E*)a.dv + ro;
+      const float sc = a.scale;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int j = dt * 4 + q4;
+          const f32x4 ok = *(const f32x4*)(pk + (j * 64 + lane) * 4);
+          const f32x4 ov = *(const f32x4*)(pv + (j * 64 + lane) * 4);
+          *(uint2*)(dkr + 32 * dt + 8 * q4 + 4 * hh) =
+              make_uint2(pack2<TT>((dkacc[dt][4 * q4] + ok[0]) * sc, (dkacc[dt][4 * q4 + 1] + ok[1]) * sc),
+                         pack2<TT>((dkacc[dt][4 * q4 + 2] + ok[2]) * sc, (dkacc[dt][4 * q4 + 3] + ok[3]) * sc));
+          *(uint2*)(dvr + 32 * dt + 8 * q4 + 4 * hh) =
+              make_uint2(pack2<TT>(dvacc[dt][4 * q4] + ov[0], dvacc[dt][4 * q4 + 1] + ov[1]),
+                         pack2<TT>(dvacc[dt][4 * q4 + 2] + ov[2], dvacc[dt][4 * q4 + 3] + ov[3]));
+        }
       }
     }
   }
@@ -499,7 +543,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   }
   if (a.Lk > 0) {
     const long long kblocks = (long long)((a.Lk + C::BK - 1) / C::BK) * a.B * a.Hkv;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<TT, D>), dim3((unsigned)kblocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<TT, D>), dim3((unsigned)kblocks), dim3(512), 0, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
