@@ -38,6 +38,7 @@ if ROOT not in sys.path:
 METRIC = "attn fwd TFLOP/s + % bf16 MFMA peak (L=2048/8192); paged decode HBM GB/s"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, published
 KV_ROTATION_BYTES = 1 << 30
 
 
@@ -417,6 +418,28 @@ def main():
             attain = min(PEAK_BF16_TFLOPS, fl / byts * PEAK_HBM_GBS / 1e3)
             detail[name]["frac_attainable"] = round(fl / ms / 1e9 / attain, 4)
             log(f"detail {name}: {detail[name]}")
+        # FP8 (e4m3) forward, bf16 output: the skill page's FP8 shape and the long
+        # causal GQA workload; fraction of the dense fp8 MFMA peak
+        for name in ("gqa8k_causal_fp8", "fp8_causal"):
+            cfg = CONFIGS[name]
+            fq, fk, fv = (t.to(dev) for t in dense_inputs(cfg))
+            fo = torch.empty(fq.shape, dtype=torch.bfloat16, device=dev)
+            fl_ = torch.empty((cfg.B, cfg.Hq, cfg.Lq), dtype=torch.float32, device=dev)
+            for _ in range(3):
+                ta.attn_fwd_fp8(fq, fk, fv, out=fo, lse=fl_, scale=cfg.scale, causal=cfg.causal, stream=stream)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(10):
+                ta.attn_fwd_fp8(fq, fk, fv, out=fo, lse=fl_, scale=cfg.scale, causal=cfg.causal, stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 10
+            fl = causal_flops(cfg.B, cfg.Hq, cfg.Lq, cfg.Lk, cfg.D, cfg.causal)
+            detail[name] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(fl / ms / 1e9, 1),
+                            "frac_fp8_mfma": round(fl / ms / 1e9 / PEAK_FP8_TFLOPS, 4)}
+            log(f"detail {name}: {detail[name]}")
+            del fq, fk, fv, fo, fl_
+
         # backward (dq, dk, dv) on the long causal GQA workload and the L=2048
         # one; algorithmic flops 2.5x the forward's (the recomputed S plus the
         # dV, dP, dK and dQ products)

@@ -164,6 +164,28 @@ int attn_fwd_paged(const void* q, const void* k_cache, const void* v_cache,
                    float scale, int causal, int window, int dtype, void* stream);
 
 /*
+ * attn_fwd_fp8 - FP8 attention forward (inference / forward only).
+ *
+ *   q    [B, Lq, Hq,  D]  float8 e4m3 (OCP e4m3fn)   k, v [B, Lk, Hkv, D]  e4m3
+ *   out  [B, Lq, Hq,  D]  bf16                       lse  [B, Hq, Lq] fp32, may be NULL
+ *
+ * The FP8 forward of the "Flash Attention" skill page, scenario 3 (inputs cast
+ * to float8_e4m3fn, forward pass only), with per-tensor descale factors:
+ * the inputs stand for q*q_descale, k*k_descale, v*v_descale, so
+ *   out = softmax(scale * q_descale * k_descale * q k^T) * (v_descale * v),
+ * with the masks, GQA mapping, empty-row rule and lse of attn_fwd (lse is that
+ * of the scaled scores).  The scores and the row sums are exact fp32 sums of
+ * the fp8 products; the probabilities enter the P*V product rounded to e4m3
+ * (3 mantissa bits), so each output element is within about
+ * 2^-4 * sum_j P_ij |v_j| of the exact value, plus its bf16 rounding.
+ * Errors as attn_fwd (D in {64, 128}).
+ */
+int attn_fwd_fp8(const void* q, const void* k, const void* v, void* out, float* lse,
+                 int B, int Hq, int Hkv, int Lq, int Lk, int D,
+                 float scale, float q_descale, float k_descale, float v_descale,
+                 int causal, int window, void* stream);
+
+/*
  * attn_bwd - gradients of attention: dq, dk, dv of L = sum(dout * out) for
  * the out = attn_fwd(q, k, v, ...) computed with the same arguments.
  *

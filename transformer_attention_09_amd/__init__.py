@@ -8,6 +8,7 @@ the C ABI declared in include/attn.h, with the same entry-point names:
     attn_decode_paged(q, k_cache, ...)      q [S,Hq,D], caches [N,16,Hkv,D]
     attn_fwd_paged(q, k_cache, ...)         q [B,Lq,Hq,D] over paged caches [N,16,Hkv,D]
     attn_bwd(q, k, v, out, dout, lse, ...)  gradients dq, dk, dv
+    attn_fwd_fp8(q, k, v, ...)              float8_e4m3fn inputs, bf16 output
     attn_bwd_workspace_size(B, Hq, Lq)
     attn_decode_paged_workspace_size(...)
     attn_status_string(status)
@@ -39,7 +40,7 @@ STATUS = {
     -7: "ATTN_ERR_HIP",
 }
 EXPORTED = ("attn_fwd", "attn_decode_paged", "attn_decode_paged_workspace_size", "attn_status_string",
-            "attn_fwd_paged", "attn_bwd", "attn_bwd_workspace_size", "attn_hbm_read_probe")
+            "attn_fwd_paged", "attn_bwd", "attn_bwd_workspace_size", "attn_fwd_fp8", "attn_hbm_read_probe")
 
 _lib = None
 _lock = threading.Lock()
@@ -78,6 +79,9 @@ def load_library() -> ctypes.CDLL:
             lib.attn_bwd.restype = i32
             lib.attn_bwd_workspace_size.argtypes = [i32, i32, i32]
             lib.attn_bwd_workspace_size.restype = sz
+            lib.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, f32, f32, f32,
+                                         i32, i32, vp]
+            lib.attn_fwd_fp8.restype = i32
             lib.attn_hbm_read_probe.argtypes = [vp, sz, vp, vp]
             lib.attn_hbm_read_probe.restype = i32
             _lib = lib
@@ -326,6 +330,46 @@ def attn_bwd(q, k, v, out, dout, lse, dq=None, dk=None, dv=None, scale: Optional
     if st != 0:
         raise AttnError(st, "attn_bwd")
     return dq, dk, dv
+
+
+def attn_fwd_fp8(q, k, v, out=None, lse=None, scale: Optional[float] = None, q_descale: float = 1.0,
+                 k_descale: float = 1.0, v_descale: float = 1.0, causal: bool = False, window: int = -1,
+                 stream=None, return_lse: bool = True):
+    """FP8 forward: q [B,Lq,Hq,D], k/v [B,Lk,Hkv,D] as torch.float8_e4m3fn; returns
+    (out bf16 [B,Lq,Hq,D], lse fp32 [B,Hq,Lq]).  The inputs stand for
+    q*q_descale, k*k_descale, v*v_descale."""
+    import torch
+
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _require_cuda(n, t)
+        if t.dtype != torch.float8_e4m3fn:
+            raise TypeError(f"{n} must be torch.float8_e4m3fn")
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
+        raise ValueError("expected q [B,Lq,Hq,D] and k, v [B,Lk,Hkv,D] of equal shape")
+    B, Lq, Hq, D = q.shape
+    Bk, Lk, Hkv, Dk = k.shape
+    if Bk != B or Dk != D:
+        raise ValueError("q, k, v disagree in batch or head dim")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    _require_cuda("out", out)
+    if out.shape != q.shape or out.dtype != torch.bfloat16:
+        raise ValueError("out must be bfloat16 shaped like q")
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _require_cuda("lse", lse)
+        if lse.shape != (B, Hq, Lq) or lse.dtype != torch.float32:
+            raise ValueError("lse must be float32 [B,Hq,Lq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    st = load_library().attn_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                     lse.data_ptr() if lse is not None else None,
+                                     B, Hq, Hkv, Lq, Lk, D, float(scale), float(q_descale), float(k_descale),
+                                     float(v_descale), int(bool(causal)), int(window), _stream_handle(stream))
+    if st != 0:
+        raise AttnError(st, "attn_fwd_fp8")
+    return out, lse
 
 
 def attn_hbm_read_probe(buf, sink, stream=None) -> None:

@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libattn.so")
-SOURCES = ["api.hip", "fwd.hip", "bwd.hip", "decode.hip", "measure.hip"]
+SOURCES = ["api.hip", "fwd.hip", "fwd_fp8.hip", "bwd.hip", "decode.hip", "measure.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -114,6 +114,41 @@ ATTN_API int attn_fwd(const void* q, const void* k, const void* v, void* out, fl
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+ATTN_API int attn_fwd_fp8(const void* q, const void* k, const void* v, void* out, float* lse,
+                          int B, int Hq, int Hkv, int Lq, int Lk, int D,
+                          float scale, float q_descale, float k_descale, float v_descale,
+                          int causal, int window, void* stream) {
+  if (B < 0 || Lq < 0 || Lk < 0 || Hq <= 0 || Hkv <= 0) return ATTN_ERR_SHAPE;
+  const bool q_empty = (B == 0 || Lq == 0), kv_empty = (B == 0 || Lk == 0);
+  if ((!q_empty && (!q || !out)) || (!kv_empty && (!k || !v))) return ATTN_ERR_NULL;
+  if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+  const float sl = scale * q_descale * k_descale;
+  if (!std::isfinite(scale) || !std::isfinite(q_descale) || !std::isfinite(k_descale) ||
+      !std::isfinite(v_descale) || !std::isfinite(sl))
+    return ATTN_ERR_SHAPE;
+  if (!supported_d(D)) return ATTN_ERR_UNSUPPORTED;
+  if (!prod_ok(B, Lq, Hq, D) || !prod_ok(B, Lk, Hkv, D)) return ATTN_ERR_SHAPE;
+  const long long n_qblocks = ((long long)Lq + attn::kPrefillBlockM - 1) / attn::kPrefillBlockM;
+  if (n_qblocks * Hq * (long long)B > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return ATTN_ERR_ALIGN;
+  if (lse && !aligned(lse, 4)) return ATTN_ERR_ALIGN;
+  if (q_empty) return ATTN_OK;
+  const int dev = check_device();
+  if (dev != ATTN_OK) return dev;
+
+  attn::F8Args a;
+  a.q = q; a.k = k; a.v = v; a.o = out; a.lse = lse;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Lq = Lq; a.Lk = Lk;
+  a.group = Hq / Hkv;
+  a.causal = causal ? 1 : 0;
+  a.window = window < 0 ? -1 : window;
+  a.scale_log2 = sl * attn::kLog2e;
+  a.v_descale = v_descale;
+  a.n_qblocks = (int)n_qblocks;
+  hipError_t e = attn::launch_fwd_fp8(a, D, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 ATTN_API int attn_fwd_paged(const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* block_table, const int32_t* ctx_lens, int block_size,
                             void* out, float* lse,

@@ -73,6 +73,23 @@ struct BwdArgs {
   int n_qblocks;
 };
 
+// FP8 forward: q, k, v e4m3 (OCP float8_e4m3fn), out bf16; scale_log2 holds
+// scale * q_descale * k_descale * log2(e), v_descale multiplies the output.
+struct F8Args {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;  // may be null
+  int B, Hq, Hkv, Lq, Lk;
+  int group;
+  int causal;
+  int window;
+  float scale_log2;
+  float v_descale;
+  int n_qblocks;
+};
+
 constexpr int kPrefillBlockM = 128;
 constexpr int kPagedBlock = 16;  // tokens per cache block (both paged entry points)
 constexpr float kLog2e = 1.44269504088896340736f;
@@ -86,6 +103,7 @@ constexpr int kDecodeWavesPerCU = 4;
 hipError_t launch_fwd(const FwdArgs& a, int D, int dtype, hipStream_t stream);
 hipError_t launch_fwd_paged(const FwdArgs& a, int D, int dtype, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, int D, int dtype, hipStream_t stream);
+hipError_t launch_fwd_fp8(const F8Args& a, int D, hipStream_t stream);
 hipError_t launch_decode(const DecArgs& a, int D, int dtype, hipStream_t stream);
 hipError_t launch_hbm_read(const void* p, size_t bytes, unsigned* sink, int cus, hipStream_t stream);
 

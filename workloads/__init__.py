@@ -17,7 +17,8 @@ Workload shapes follow the pages:
 Recipe (identical for every consumer):
   * rng = numpy.random.default_rng(seed);
   * dense workloads draw q, k, v in that order as float32 standard normals
-    and cast them to fp16/bf16 with round-to-nearest-even (torch's cast);
+    and cast them to fp16/bf16/float8_e4m3fn with round-to-nearest-even
+    (torch's cast);
   * the paged workload draws ctx_lens (integers, inclusive range), then the
     physical-block permutation, then q, then the K pool, then the V pool;
   * the paged prefill workload (Lq new tokens per sequence, the last Lq
@@ -32,7 +33,7 @@ from typing import Optional
 import numpy as np
 import torch
 
-DTYPES = {"fp16": torch.float16, "bf16": torch.bfloat16}
+DTYPES = {"fp16": torch.float16, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -114,6 +115,10 @@ CONFIGS = {
     "gqa8k_causal": DenseConfig("gqa8k_causal", 1, 32, 8, 8192, 8192, 128, "bf16", True, -1, 5),
     "gqa8k_window": DenseConfig("gqa8k_window", 1, 32, 8, 8192, 8192, 128, "bf16", True, 4096, 5),
     "paged_decode": PagedConfig("paged_decode", 64, 12, 2, 128, "bf16", 512, 4096, 16, 6),
+    # FP8 (e4m3fn) forward: the [2, 4096, 32, 64] causal shape of the skill
+    # page's FP8 scenario, and the long causal GQA workload in fp8
+    "fp8_causal": DenseConfig("fp8_causal", 2, 32, 32, 4096, 4096, 64, "fp8", True, -1, 8),
+    "gqa8k_causal_fp8": DenseConfig("gqa8k_causal_fp8", 1, 32, 8, 8192, 8192, 128, "fp8", True, -1, 5),
     # chunked prefill on the same model shape: 512 new tokens per sequence
     "paged_prefill": PrefillConfig("paged_prefill", 16, 512, 12, 2, 128, "bf16", 512, 4096, 16, True, 7),
 }
