@@ -219,3 +219,32 @@ def test_bwd_valid_args_without_gpu_report_device():
     if torch.cuda.is_available():
         pytest.skip("a GPU is present: valid arguments would launch on the fake address")
     assert _bwd() == DEV
+
+
+def _fp8(**kw):
+    a = dict(q=P, k=P, v=P, out=P, lse=None, B=1, Hq=4, Hkv=2, Lq=16, Lk=16, D=64, scale=0.125, qd=1.0, kd=1.0,
+             vd=1.0, causal=0, window=-1)
+    a.update(kw)
+    return ta.load_library().attn_fwd_fp8(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                                          a["Lq"], a["Lk"], a["D"], a["scale"], a["qd"], a["kd"], a["vd"],
+                                          a["causal"], a["window"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(k=None), NULL), (dict(v=None), NULL), (dict(out=None), NULL),
+    (dict(B=-1), SHAPE), (dict(Lk=-1), SHAPE), (dict(Hq=6, Hkv=4), SHAPE),
+    (dict(scale=float("nan")), SHAPE), (dict(qd=float("inf")), SHAPE), (dict(vd=float("nan")), SHAPE),
+    (dict(kd=3e38, scale=3e38), SHAPE),
+    (dict(D=96), UNSUP), (dict(D=256), UNSUP),
+    (dict(q=P_MIS), ALIGN), (dict(v=P + 4), ALIGN), (dict(out=P + 2), ALIGN), (dict(lse=P + 1), ALIGN),
+    (dict(B=0), OK), (dict(Lq=0), OK),
+])
+def test_fp8_validation(kw, code):
+    assert _fp8(**kw) == code
+
+
+def test_fp8_valid_args_without_gpu_report_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: valid arguments would launch on the fake address")
+    assert _fp8() == DEV
