@@ -26,7 +26,10 @@ Readings where the pages are silent (each listed in the design doc):
   * lse is the natural log of the row's sum of exp(scaled scores), the
     "small normalisation statistics" of section 3 of the self-attention page;
   * a row with no visible key gets out = 0 and lse = -inf;
-  * the scale is used as the float32 value a GPU kernel receives.
+  * the scale is used as the float32 value a GPU kernel receives;
+  * dropout (oracle/dropout.py) drops normalised probabilities, keeps each
+    with probability 1 - p, scales the kept ones by 1 / (1 - p), and draws
+    its decisions from Philox4x32-10 at a fixed per-element counter.
 
 Parity status of every function here is recorded in tests/test_oracle.py
 (all functions are pinned; none is "parity unpinned").
@@ -43,4 +46,11 @@ from .core import (  # noqa: F401
     prefill_paged,
     row_softmax,
     split_merge_attention,
+)
+from .dropout import (  # noqa: F401
+    attention_dropout,
+    attention_dropout_backward,
+    dropout_keep,
+    dropout_threshold,
+    philox4x32,
 )

@@ -574,3 +574,218 @@ def test_p13_backward_gqa_is_sum_over_expanded_heads():
     np.testing.assert_allclose(dq, dq1, atol=TIGHT)
     np.testing.assert_allclose(dk, dk1.reshape(B, L, Hkv, Hq // Hkv, D).sum(axis=3), atol=TIGHT)
     np.testing.assert_allclose(dv, dv1.reshape(B, L, Hkv, Hq // Hkv, D).sum(axis=3), atol=TIGHT)
+
+
+# ---------------------------------------------------------------- P14: dropout
+# The generator is Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC 2011); the
+# oracle's numpy copy is pinned against rocRAND's engine, a library
+# implementation compiled here for the host from its header.
+
+import shutil
+import subprocess
+
+_ROCRAND_HDR = "/opt/rocm/include/rocrand/rocrand_philox4x32_10.h"
+
+
+def build_philox_ref(workdir):
+    """Compile tests/philox_ref.cpp (rocRAND's engine) into workdir and return
+    run(mode, rows) -> int64 array of its output lines; None without g++ or
+    the header."""
+    gxx = shutil.which("g++")
+    if gxx is None or not os.path.exists(_ROCRAND_HDR):
+        return None
+    exe = os.path.join(str(workdir), "philox_ref")
+    subprocess.run([gxx, "-O1", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+                    os.path.join(HERE, "philox_ref.cpp"), "-o", exe], check=True)
+
+    def run(mode, rows):
+        text = "".join(" ".join(str(int(x)) for x in r) + "\n" for r in rows)
+        res = subprocess.run([exe, mode], input=text, capture_output=True, text=True, check=True)
+        return np.array([[int(w) for w in line.split()] for line in res.stdout.splitlines()], dtype=np.int64)
+    return run
+
+
+@pytest.fixture(scope="module")
+def philox_ref(tmp_path_factory):
+    run = build_philox_ref(tmp_path_factory.mktemp("philox"))
+    if run is None:
+        pytest.skip("g++ or rocRAND's Philox header not available")
+    return run
+
+
+def _philox_cases(n=300, seed=14):
+    r = np.random.default_rng(seed)
+    top = 2 ** 32 - 1
+    rows = [(0, 0, 0, 0, 0, 0), (top, top, top, 2 ** 30 - 1, top, top), (1, 0, 0, 0, 0, 0),
+            (0, 0, 1, 0, 0, 0), (0, 0, 0, 1, 0, 0), (0, 0, 0, 0, 1, 0), (0, 0, 0, 0, 0, 1)]
+    for _ in range(n):
+        rows.append((r.integers(0, 2 ** 32), r.integers(0, 2 ** 32), r.integers(0, 2 ** 32),
+                     r.integers(0, 2 ** 30), r.integers(0, 2 ** 32), r.integers(0, 2 ** 32)))
+    return np.array(rows, dtype=np.int64)
+
+
+def test_p14_philox_matches_library_engine(philox_ref):
+    cases = _philox_cases()
+    want = philox_ref("words", cases)
+    got = oracle.philox4x32(cases[:, 2:6], (cases[:, 0], cases[:, 1])).astype(np.int64)
+    assert np.array_equal(got, want)
+
+
+def test_p14_keep_convention_matches_library_engine(philox_ref):
+    # element (bh, i, j) against the engine addressed per element, over rows and
+    # keys that cross 4-key groups, large row and key indexes, offsets and seeds
+    for (seed, off, p, bh, rows, Lk) in [(0, 0, 0.1, 0, [0, 1, 5], 13),
+                                          (0x1234567890ABCDEF, 77, 0.5, 37, [0, 9, 1000, 65535], 70),
+                                          (2 ** 64 - 1, 2 ** 32 - 1, 0.9, 2 ** 20 + 3, [3, 2 ** 29], 9)]:
+        thr = oracle.dropout_threshold(p)
+        keep = oracle.dropout_keep(bh, rows, Lk, p, seed, off)
+        qs = [(seed, off, thr, bh, i, j) for i in rows for j in range(Lk)]
+        want = philox_ref("keep", qs).reshape(len(rows), Lk).astype(bool)
+        assert np.array_equal(keep, want)
+
+
+def test_p14_threshold_and_validation():
+    assert oracle.dropout_threshold(0.0) == 0
+    assert oracle.dropout_threshold(0.5) == 2 ** 31
+    assert oracle.dropout_threshold(0.25) == 2 ** 30
+    p32 = float(np.float32(0.1))
+    assert oracle.dropout_threshold(0.1) == math.floor(p32 * 2 ** 32)
+    for bad in (1.0, -0.01, 1.5, float("nan")):
+        with pytest.raises(ValueError):
+            oracle.dropout_threshold(bad)
+
+
+@pytest.mark.parametrize("p", [0.1, 0.5, 0.9])
+def test_p14_keep_rate_is_one_minus_p(p):
+    # 2 heads x 300 rows x 700 keys = 420,000 independent decisions: the kept
+    # fraction must lie within 5 binomial standard deviations of 1 - p, in
+    # total and for each of the four words of a Philox output
+    keep = np.concatenate([oracle.dropout_keep(bh, np.arange(300), 700, p, 99, 3) for bh in (0, 1)])
+    n = keep.size
+    sd = math.sqrt(p * (1 - p) / n)
+    assert abs(keep.mean() - (1 - p)) < 5 * sd
+    for w in range(4):
+        kw = keep[:, w::4]
+        assert abs(kw.mean() - (1 - p)) < 5 * math.sqrt(p * (1 - p) / kw.size)
+    # neighbouring decisions are uncorrelated (lag-1 along keys and rows)
+    x = keep.astype(float) - keep.mean()
+    for a, b in ((x[:, 1:], x[:, :-1]), (x[1:], x[:-1])):
+        corr = (a * b).mean() / x.var()
+        assert abs(corr) < 5 / math.sqrt(a.size)
+
+
+@pytest.mark.parametrize("causal,window", MASKS)
+def test_p14_zero_probability_is_plain_attention(causal, window):
+    q, k, v = small_case(seed=140)
+    out, lse = oracle.attention_dropout(q, k, v, 0.4, causal, window, p=0.0, seed=5, offset=1)
+    ref, rl = oracle.attention(q, k, v, 0.4, causal, window)
+    assert np.array_equal(out, ref) and np.array_equal(lse, rl)
+
+
+def test_p14_identity_values_expose_dropped_probabilities():
+    # with V = I (one value dimension per key) row i of the output is
+    # P_i * keep_i / (1 - p): the mask multiplies the normalised probabilities
+    r = np.random.default_rng(141)
+    B, Hq, Hkv, Lq, Lk = 1, 2, 1, 11, 16
+    q = r.standard_normal((B, Lq, Hq, Lk))
+    k = r.standard_normal((B, Lk, Hkv, Lk))
+    v = np.eye(Lk)[None, :, None, :]
+    p, seed, off = 0.3, 1234, 9
+    out, lse = oracle.attention_dropout(q, k, v, 0.5, True, -1, p, seed, off)
+    ref, rl = oracle.attention(q, k, v, 0.5, True, -1)  # = P itself
+    assert np.array_equal(lse, rl)
+    for h in range(Hq):
+        keep = oracle.dropout_keep(h, np.arange(Lq), Lk, p, seed, off)
+        want = np.where(keep, ref[0, :, h, :], 0.0) / (1 - float(np.float32(p)))
+        np.testing.assert_allclose(out[0, :, h, :], want, rtol=1e-14, atol=1e-15)
+    assert (out == 0).any() and (out > 0).any()
+
+
+def test_p14_dropout_is_unbiased_over_seeds():
+    # inverted dropout: averaged over independent draws the output tends to the
+    # plain output (each element within 6 standard errors of the sample mean)
+    q, k, v = small_case(B=1, Hq=2, Hkv=1, Lq=6, Lk=10, D=4, seed=142)
+    ref, _ = oracle.attention(q, k, v, 0.7, False, -1)
+    draws = np.stack([oracle.attention_dropout(q, k, v, 0.7, False, -1, 0.5, s, 0)[0] for s in range(600)])
+    mean, se = draws.mean(axis=0), draws.std(axis=0) / math.sqrt(len(draws))
+    assert np.all(np.abs(mean - ref) <= 6 * se + 1e-12)
+
+
+def test_p14_dropout_rows_subset_matches_full():
+    q, k, v = small_case(Lq=20, Lk=23, seed=143)
+    out, lse = oracle.attention_dropout(q, k, v, 0.3, True, 4, 0.2, 77, 5)
+    rows = [0, 3, 19, 7]
+    o2, l2 = oracle.attention_dropout(q, k, v, 0.3, True, 4, 0.2, 77, 5, rows=rows)
+    assert np.array_equal(o2, out[:, rows]) and np.array_equal(l2, lse[:, :, rows])
+
+
+def _torch_dropout_grads(q, k, v, do, sc, causal, window, p, seed, off):
+    """torch autograd (float64, CPU) of sum(do * ((softmax(S) * M) @ V)) with
+    the mask M = keep / (1 - p) held fixed."""
+    B, Lq, Hq, D = q.shape
+    Lk, Hkv = k.shape[1], k.shape[2]
+    grp = Hq // Hkv
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    ok = torch.tensor(oracle.allowed_mask(Lq, Lk, causal, window))
+    loss = 0.0
+    for b in range(B):
+        for h in range(Hq):
+            S = float(np.float32(sc)) * tq[b, :, h] @ tk[b, :, h // grp].T
+            S = S.masked_fill(~ok, float("-inf"))
+            P = torch.softmax(S, dim=1).nan_to_num(0.0)
+            M = torch.tensor(np.where(oracle.dropout_keep(b * Hq + h, np.arange(Lq), Lk, p, seed, off),
+                                      1.0 / (1.0 - float(np.float32(p))), 0.0))
+            loss = loss + (torch.tensor(do[b, :, h]) * ((P * M) @ tv[b, :, h // grp])).sum()
+    loss.backward()
+    return tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
+
+
+@pytest.mark.parametrize("causal,window", [(False, -1), (True, -1), (True, 2)])
+def test_p14_dropout_backward_matches_torch_autograd(causal, window):
+    r = np.random.default_rng(144)
+    q = r.standard_normal((2, 7, 4, 6))
+    k = r.standard_normal((2, 9, 2, 6))
+    v = r.standard_normal((2, 9, 2, 6))
+    do = r.standard_normal(q.shape)
+    got = oracle.attention_dropout_backward(q, k, v, do, 0.45, causal, window, 0.3, 31, 2)
+    want = _torch_dropout_grads(q, k, v, do, 0.45, causal, window, 0.3, 31, 2)
+    for g, w in zip(got, want):
+        np.testing.assert_allclose(g, w, rtol=1e-11, atol=1e-12)
+
+
+def test_p14_dropout_backward_zero_probability_is_plain_backward():
+    r = np.random.default_rng(145)
+    q = r.standard_normal((1, 5, 2, 4))
+    k = r.standard_normal((1, 8, 1, 4))
+    v = r.standard_normal((1, 8, 1, 4))
+    do = r.standard_normal(q.shape)
+    got = oracle.attention_dropout_backward(q, k, v, do, 0.6, True, -1, 0.0, 3, 0)
+    want = oracle.attention_backward(q, k, v, do, 0.6, True, -1)
+    for g, w in zip(got, want):
+        np.testing.assert_allclose(g, w, rtol=0, atol=TIGHT)
+
+
+def test_p14_dropout_backward_matches_finite_differences():
+    r = np.random.default_rng(146)
+    q = r.standard_normal((1, 4, 2, 3))
+    k = r.standard_normal((1, 5, 1, 3))
+    v = r.standard_normal((1, 5, 1, 3))
+    do = r.standard_normal(q.shape)
+    args = (0.8, True, 1, 0.4, 8, 1)
+
+    def loss(q_, k_, v_):
+        return float((do * oracle.attention_dropout(q_, k_, v_, *args)[0]).sum())
+    grads = oracle.attention_dropout_backward(q, k, v, do, *args)
+    eps = 1e-6
+    for idx, x in enumerate((q, k, v)):
+        num = np.zeros_like(x)
+        for pos in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[pos] += eps
+            xm[pos] -= eps
+            a = [q, k, v]
+            a[idx] = xp
+            lp = loss(*a)
+            a[idx] = xm
+            num[pos] = (lp - loss(*a)) / (2 * eps)
+        np.testing.assert_allclose(grads[idx], num, rtol=1e-6, atol=1e-7)
