@@ -440,6 +440,32 @@ def main():
             log(f"detail {name}: {detail[name]}")
             del fq, fk, fv, fo, fl_
 
+        # forward with dropout (p = 0.1, the skill page's scenario 2 value) on the
+        # long causal GQA workload, beside the plain forward of the same launch shape
+        dcfg = CONFIGS["gqa8k_causal"]
+        dq_, dk_, dv_ = (t.to(dev) for t in dense_inputs(dcfg))
+        do_ = torch.empty_like(dq_)
+        dl_ = torch.empty((dcfg.B, dcfg.Hq, dcfg.Lq), dtype=torch.float32, device=dev)
+        for _ in range(3):
+            ta.attn_fwd_dropout(dq_, dk_, dv_, 0.1, 1234, 0, out=do_, lse=dl_, scale=dcfg.scale, causal=True,
+                                stream=stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for it in range(10):
+            ta.attn_fwd_dropout(dq_, dk_, dv_, 0.1, 1234, it, out=do_, lse=dl_, scale=dcfg.scale, causal=True,
+                                stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 10
+        ms_plain = time_fwd(dcfg)
+        fl = causal_flops(dcfg.B, dcfg.Hq, dcfg.Lq, dcfg.Lk, dcfg.D, True)
+        detail["dropout_gqa8k_causal"] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(fl / ms / 1e9, 1),
+                                          "frac_mfma": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+                                          "plain_us": round(ms_plain * 1e3, 2),
+                                          "time_vs_plain": round(ms / ms_plain, 3)}
+        log(f"detail dropout_gqa8k_causal: {detail['dropout_gqa8k_causal']}")
+        del dq_, dk_, dv_, do_, dl_
+
         # backward (dq, dk, dv) on the long causal GQA workload and the L=2048
         # one; algorithmic flops 2.5x the forward's (the recomputed S plus the
         # dV, dP, dK and dQ products)

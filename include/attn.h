@@ -92,6 +92,35 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
              float scale, int causal, int window, int dtype, void* stream);
 
 /*
+ * attn_fwd_dropout - attn_fwd with dropout on the attention probabilities
+ * (the training-time forward; the dropout_p argument of the flash-attn call on
+ * the «Flash Attention» page, quick start and scenario 2).
+ *
+ * Same tensors, masks and errors as attn_fwd, plus:
+ *   dropout_p  probability of dropping each probability, 0 <= dropout_p < 1
+ *              (else ATTN_ERR_SHAPE; 0 gives attn_fwd's result);
+ *   seed       64-bit key of the random generator;
+ *   offset     32-bit stream selector (e.g. the training step), so one seed
+ *              can serve many calls without reusing a mask.
+ *
+ *   out[b,i,h,:] = sum_j P[i,j] * keep(b,h,i,j) * v[b,j,g,:] / (1 - dropout_p)
+ *
+ * with P the row softmax of attn_fwd; lse is attn_fwd's (the undropped row
+ * statistic), which attn_bwd_dropout needs.  keep(b,h,i,j) is 1 iff word j%4
+ * of Philox4x32-10 (Salmon, Moraes, Dror, Shaw: "Parallel Random Numbers:
+ * As Easy as 1, 2, 3", SC 2011) at the counter (j/4, i, b*Hq + h, offset)
+ * under the key (seed mod 2^32, seed / 2^32) is >= floor(dropout_p * 2^32),
+ * so each probability is kept with probability 1 - dropout_p (exactly, for
+ * dropout_p a multiple of 2^-32), independently of the others, and any
+ * element's decision can be recomputed on its own (the backward does).
+ * 1 / (1 - dropout_p) is applied in fp32 with the output normalisation.
+ */
+int attn_fwd_dropout(const void* q, const void* k, const void* v, void* out, float* lse,
+                     int B, int Hq, int Hkv, int Lq, int Lk, int D,
+                     float scale, int causal, int window,
+                     float dropout_p, uint64_t seed, uint32_t offset, int dtype, void* stream);
+
+/*
  * attn_decode_paged - one new query token per sequence against its paged
  * KV cache.
  *

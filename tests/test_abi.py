@@ -248,3 +248,34 @@ def test_fp8_valid_args_without_gpu_report_device():
     if torch.cuda.is_available():
         pytest.skip("a GPU is present: valid arguments would launch on the fake address")
     assert _fp8() == DEV
+
+
+def _drop(**kw):
+    a = dict(q=P, k=P, v=P, out=P, lse=None, B=1, Hq=4, Hkv=2, Lq=16, Lk=16, D=64, scale=0.125,
+             causal=0, window=-1, p=0.1, seed=1, offset=0, dtype=1)
+    a.update(kw)
+    return ta.load_library().attn_fwd_dropout(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Hq"],
+                                              a["Hkv"], a["Lq"], a["Lk"], a["D"], a["scale"], a["causal"],
+                                              a["window"], a["p"], a["seed"], a["offset"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(out=None), NULL), (dict(v=None), NULL),
+    (dict(B=-1), SHAPE), (dict(Hq=6, Hkv=4), SHAPE), (dict(scale=float("inf")), SHAPE),
+    (dict(p=1.0), SHAPE), (dict(p=1.5), SHAPE), (dict(p=-0.1), SHAPE), (dict(p=float("nan")), SHAPE),
+    (dict(p=float("inf")), SHAPE),
+    (dict(D=96), UNSUP), (dict(dtype=2), UNSUP),
+    (dict(q=P_MIS), ALIGN), (dict(lse=P + 1), ALIGN),
+    (dict(B=0), OK), (dict(Lq=0), OK), (dict(Lq=0, p=0.0), OK), (dict(B=0, seed=2 ** 64 - 1, offset=2 ** 32 - 1), OK),
+])
+def test_fwd_dropout_validation(kw, code):
+    assert _drop(**kw) == code
+
+
+def test_fwd_dropout_valid_args_without_gpu_report_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: valid arguments would launch on the fake address")
+    assert _drop() == DEV
+    assert _drop(p=0.0) == DEV
+    assert _drop(p=0.99999994) == DEV  # the largest float below 1

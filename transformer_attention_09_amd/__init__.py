@@ -5,6 +5,7 @@ module only marshals torch tensors (device memory and the current stream) into
 the C ABI declared in include/attn.h, with the same entry-point names:
 
     attn_fwd(q, k, v, ...)                  q [B,Lq,Hq,D], k/v [B,Lk,Hkv,D]
+    attn_fwd_dropout(q, k, v, p, seed, ...) the same with dropout on the probabilities
     attn_decode_paged(q, k_cache, ...)      q [S,Hq,D], caches [N,16,Hkv,D]
     attn_fwd_paged(q, k_cache, ...)         q [B,Lq,Hq,D] over paged caches [N,16,Hkv,D]
     attn_bwd(q, k, v, out, dout, lse, ...)  gradients dq, dk, dv
@@ -40,7 +41,8 @@ STATUS = {
     -7: "ATTN_ERR_HIP",
 }
 EXPORTED = ("attn_fwd", "attn_decode_paged", "attn_decode_paged_workspace_size", "attn_status_string",
-            "attn_fwd_paged", "attn_bwd", "attn_bwd_workspace_size", "attn_fwd_fp8", "attn_hbm_read_probe")
+            "attn_fwd_paged", "attn_bwd", "attn_bwd_workspace_size", "attn_fwd_fp8", "attn_hbm_read_probe",
+            "attn_fwd_dropout")
 
 _lib = None
 _lock = threading.Lock()
@@ -84,6 +86,9 @@ def load_library() -> ctypes.CDLL:
             lib.attn_fwd_fp8.restype = i32
             lib.attn_hbm_read_probe.argtypes = [vp, sz, vp, vp]
             lib.attn_hbm_read_probe.restype = i32
+            lib.attn_fwd_dropout.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32,
+                                             f32, ctypes.c_uint64, ctypes.c_uint32, i32, vp]
+            lib.attn_fwd_dropout.restype = i32
             _lib = lib
     return _lib
 
@@ -123,13 +128,8 @@ def _require_cuda(name, t):
         raise ValueError(f"{name} must be contiguous")
 
 
-def attn_fwd(q, k, v, out=None, lse=None, scale: Optional[float] = None, causal: bool = False,
-             window: int = -1, stream=None, return_lse: bool = True):
-    """Fused attention forward; returns (out, lse) (lse None if not requested).
-
-    q [B,Lq,Hq,D], k/v [B,Lk,Hkv,D]; scale defaults to 1/sqrt(D); window < 0
-    disables the sliding window; causal masking is aligned bottom-right.
-    """
+def _fwd_tensors(q, k, v, out, lse, scale, return_lse):
+    """Check the dense forward's tensors; allocate out/lse if not given."""
     import torch
 
     for n, t in (("q", q), ("k", k), ("v", v)):
@@ -153,12 +153,44 @@ def attn_fwd(q, k, v, out=None, lse=None, scale: Optional[float] = None, causal:
             raise ValueError("lse must be float32 [B,Hq,Lq]")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    return out, lse, (B, Hq, Hkv, Lq, Lk, D), float(scale)
+
+
+def attn_fwd(q, k, v, out=None, lse=None, scale: Optional[float] = None, causal: bool = False,
+             window: int = -1, stream=None, return_lse: bool = True):
+    """Fused attention forward; returns (out, lse) (lse None if not requested).
+
+    q [B,Lq,Hq,D], k/v [B,Lk,Hkv,D]; scale defaults to 1/sqrt(D); window < 0
+    disables the sliding window; causal masking is aligned bottom-right.
+    """
+    out, lse, dims, scale = _fwd_tensors(q, k, v, out, lse, scale, return_lse)
     st = load_library().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                  lse.data_ptr() if lse is not None else None,
-                                 B, Hq, Hkv, Lq, Lk, D, float(scale), int(bool(causal)), int(window),
+                                 *dims, scale, int(bool(causal)), int(window),
                                  _dtype_code(q), _stream_handle(stream))
     if st != 0:
         raise AttnError(st, "attn_fwd")
+    return out, lse
+
+
+def attn_fwd_dropout(q, k, v, dropout_p: float, seed: int, offset: int = 0, out=None, lse=None,
+                     scale: Optional[float] = None, causal: bool = False, window: int = -1,
+                     stream=None, return_lse: bool = True):
+    """attn_fwd with dropout on the probabilities; returns (out, lse).
+
+    Each probability is kept with probability 1 - dropout_p and the kept ones
+    are scaled by 1 / (1 - dropout_p); the decisions come from Philox4x32-10
+    keyed by the 64-bit seed, with the 32-bit offset selecting the stream
+    (contract in include/attn.h).  lse is the undropped one.
+    """
+    out, lse, dims, scale = _fwd_tensors(q, k, v, out, lse, scale, return_lse)
+    st = load_library().attn_fwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                         lse.data_ptr() if lse is not None else None,
+                                         *dims, scale, int(bool(causal)), int(window),
+                                         float(dropout_p), int(seed) & (2 ** 64 - 1), int(offset) & 0xFFFFFFFF,
+                                         _dtype_code(q), _stream_handle(stream))
+    if st != 0:
+        raise AttnError(st, "attn_fwd_dropout")
     return out, lse
 
 

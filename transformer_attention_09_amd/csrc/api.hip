@@ -79,15 +79,20 @@ ATTN_API const char* attn_status_string(int status) {
   }
 }
 
-ATTN_API int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
-                      int B, int Hq, int Hkv, int Lq, int Lk, int D,
-                      float scale, int causal, int window, int dtype, void* stream) {
+namespace {
+
+// Validation and launch shared by attn_fwd and attn_fwd_dropout.
+int fwd_dense(const void* q, const void* k, const void* v, void* out, float* lse,
+              int B, int Hq, int Hkv, int Lq, int Lk, int D,
+              float scale, int causal, int window, int dtype, void* stream,
+              bool drop, float dropout_p, uint64_t seed, uint32_t offset) {
   if (B < 0 || Lq < 0 || Lk < 0 || Hq <= 0 || Hkv <= 0) return ATTN_ERR_SHAPE;
   // A pointer may be NULL only when the tensor it describes is empty.
   const bool q_empty = (B == 0 || Lq == 0), kv_empty = (B == 0 || Lk == 0);
   if ((!q_empty && (!q || !out)) || (!kv_empty && (!k || !v))) return ATTN_ERR_NULL;
   if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
   if (!std::isfinite(scale)) return ATTN_ERR_SHAPE;
+  if (drop && !(dropout_p >= 0.f && dropout_p < 1.f)) return ATTN_ERR_SHAPE;  // NaN fails too
   if (!supported_d(D) || !supported_dtype(dtype)) return ATTN_ERR_UNSUPPORTED;
   if (!prod_ok(B, Lq, Hq, D) || !prod_ok(B, Lk, Hkv, D)) return ATTN_ERR_SHAPE;
   const long long n_qblocks = ((long long)Lq + attn::kPrefillBlockM - 1) / attn::kPrefillBlockM;
@@ -110,8 +115,32 @@ ATTN_API int attn_fwd(const void* q, const void* k, const void* v, void* out, fl
   a.ctx_lens = nullptr;
   a.max_blocks_per_seq = 0;
   a.num_blocks = 0;
-  hipError_t e = attn::launch_fwd(a, D, dtype, (hipStream_t)stream);
+  // threshold floor(p * 2^32): exact in double, below 2^32 for p < 1
+  a.drop_thr = drop ? (uint32_t)std::floor((double)dropout_p * 4294967296.0) : 0u;
+  a.drop_scale = drop ? (float)(1.0 / (1.0 - (double)dropout_p)) : 1.f;
+  a.seed_lo = (uint32_t)seed;
+  a.seed_hi = (uint32_t)(seed >> 32);
+  a.drop_offset = offset;
+  hipError_t e = drop ? attn::launch_fwd_dropout(a, D, dtype, (hipStream_t)stream)
+                      : attn::launch_fwd(a, D, dtype, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // namespace
+
+ATTN_API int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                      int B, int Hq, int Hkv, int Lq, int Lk, int D,
+                      float scale, int causal, int window, int dtype, void* stream) {
+  return fwd_dense(q, k, v, out, lse, B, Hq, Hkv, Lq, Lk, D, scale, causal, window, dtype, stream,
+                   false, 0.f, 0u, 0u);
+}
+
+ATTN_API int attn_fwd_dropout(const void* q, const void* k, const void* v, void* out, float* lse,
+                              int B, int Hq, int Hkv, int Lq, int Lk, int D,
+                              float scale, int causal, int window,
+                              float dropout_p, uint64_t seed, uint32_t offset, int dtype, void* stream) {
+  return fwd_dense(q, k, v, out, lse, B, Hq, Hkv, Lq, Lk, D, scale, causal, window, dtype, stream,
+                   true, dropout_p, seed, offset);
 }
 
 ATTN_API int attn_fwd_fp8(const void* q, const void* k, const void* v, void* out, float* lse,

@@ -258,6 +258,25 @@ __device__ __forceinline__ float sum_xor16(float x) {
 
 constexpr float kLn2 = 0.69314718055994530942f;
 
+// Philox4x32-10, the counter-based generator of Salmon, Moraes, Dror and
+// Shaw ("Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011): ten rounds,
+// each taking the 32x32->64-bit products of word 0 by 0xD2511F53 and of word
+// 2 by 0xCD9E8D57, and outputting (hi(w2-product) ^ x1 ^ k0, lo(w2-product),
+// hi(w0-product) ^ x3 ^ k1, lo(w0-product)); the key grows by the Weyl
+// increments (0x9E3779B9, 0xBB67AE85) after every round.  The key is
+// wave-uniform where it is used, so its schedule runs on the scalar unit.
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
+    c = make_uint4((uint32_t)(p1 >> 32) ^ c.y ^ k0, (uint32_t)p1, (uint32_t)(p0 >> 32) ^ c.w ^ k1, (uint32_t)p0);
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c;
+}
+
 // f(std::integral_constant<int, i>) for i = 0..N-1, expanded at compile time,
 // so that per-iteration indices (register array slots, schedule positions)
 // are constants.

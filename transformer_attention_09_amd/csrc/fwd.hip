@@ -88,7 +88,7 @@ __device__ __forceinline__ int v_swz(int r) {
 constexpr float kRescaleThreshold = 8.0f;
 
 
-template <typename TT, int D, bool PAGED>
+template <typename TT, int D, bool PAGED, bool DROP>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   using C = FwdCfg<D>;
   using E = typename TT::elem;
@@ -179,6 +179,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   }
   const int wr_lo = q0 + wave * 32;
   const int wr_hi = min(wr_lo + 31, a.Lq - 1);
+  // Dropout: the Philox counter of this row's keys j..j+3 (j = 4c) is
+  // (c, qi, b*Hq + hq, offset); see philox4x32_10.
+  const uint32_t drop_bh = (uint32_t)(b * a.Hq + hq);
 
   // ---- per-lane LDS element offsets inside a tile
   int koff[C::KSTEPS];  // K operand of k-step s, first 32-key half (+32*D for the second)
@@ -297,6 +300,29 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     return max_xor32(mx);
   };
 
+  // Dropout decisions of a tile's 32 elements in this lane, bit e for
+  // element e.  Element e is key 8*(e/4) + 4*hh + e%4 of the tile, so the
+  // elements 4g..4g+3 are the four words of one Philox call whose counter
+  // word 0 is 16*t + 2*g + hh.
+  // The empty asm statement makes the counter and the key opaque at each
+  // call, so the compiler can neither hoist the parts of the rounds that do
+  // not depend on the tile out of the key loop nor turn the products of
+  // word 0 into induction variables: either would keep values live across
+  // the loop, which has no registers to spare.
+  auto draw_tile = [&](int t) -> uint32_t {
+    uint32_t bits = 0u;
+    const uint32_t th = a.drop_thr;
+    uint32_t c0 = (uint32_t)(16 * t + hh), row = (uint32_t)qi, bh = drop_bh, k0 = a.seed_lo, k1 = a.seed_hi;
+    asm volatile("" : "+v"(c0), "+v"(row), "+s"(bh), "+s"(k0), "+s"(k1));
+#pragma unroll
+    for (int g4 = 0; g4 < 8; ++g4) {
+      const uint4 r = philox4x32_10(make_uint4(c0 + 2 * g4, row, bh, a.drop_offset), k0, k1);
+      bits |= ((r.x >= th ? 1u : 0u) | (r.y >= th ? 2u : 0u) | (r.z >= th ? 4u : 0u) | (r.w >= th ? 8u : 0u)) << (4 * g4);
+    }
+    return bits;
+  };
+  uint32_t kbits = 0u;  // decisions of the current tile (dropout only)
+
   f32x16 oacc[C::DB];
 #pragma unroll
   for (int d = 0; d < C::DB; ++d) oacc[d] = f32x16{};
@@ -371,6 +397,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     float px[32];  // probabilities in flight: exponent argument, then value
     uint32_t pw[4][4];
     V8 vop[4][G];
+
     auto read_v = [&](int st) {
 #pragma unroll
       for (int d = 0; d < G; ++d) {
@@ -390,6 +417,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       // keep the sum here, between the MFMAs, instead of letting it sink
       // below the loop's barrier where nothing overlaps it
       asm volatile("" : "+v"(rs));
+      if constexpr (DROP) px[e] = (kbits >> e) & 1u ? px[e] : 0.f;  // the row sum keeps every probability
       if (e & 1) pw[e >> 3][(e & 7) >> 1] = pack2<TT>(px[e - 1], px[e]);
     };
     __builtin_amdgcn_sched_barrier(0);
@@ -459,6 +487,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     }
     scur[0] = snext[0];
     scur[1] = snext[1];
+    // The next tile's dropout decisions, while its loads complete (few
+    // registers are live here).
+    if constexpr (DROP) kbits = draw_tile(t + 1);
     wait_vmem();
     __syncthreads();
     __builtin_amdgcn_s_setprio(0);
@@ -495,6 +526,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     }
     if (!tile_full(t_lo)) mask_tile(t_lo, scur);
     mx_cur = row_max(scur);
+    if constexpr (DROP) kbits = draw_tile(t_lo);
     __syncthreads();  // K(t_lo)'s buffer is refilled by the first tile
   }
   for (int t = t_lo; t < t_hi; t += 2) {
@@ -504,7 +536,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 
   // ---- epilogue: normalise, store O in the input type, and the log-sum-exp
   const float lt = sum_xor32(l_run);
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if constexpr (DROP) inv *= a.drop_scale;
   if (qi < a.Lq) {
     E* orow = (E*)a.o + ((size_t)((size_t)b * a.Lq + qi) * a.Hq + hq) * D;
 #pragma unroll
@@ -521,10 +554,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   }
 }
 
-template <typename TT, int D, bool PAGED>
+template <typename TT, int D, bool PAGED, bool DROP = false>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   const long long blocks = (long long)a.n_qblocks * a.Hq * a.B;
-  hipLaunchKernelGGL((fwd_kernel<TT, D, PAGED>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((fwd_kernel<TT, D, PAGED, DROP>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -532,6 +565,12 @@ hipError_t launch_fwd(const FwdArgs& a, int D, int dtype, hipStream_t stream) {
   if (dtype == 1)
     return D == 128 ? launch_fwd_t<BF16, 128, false>(a, stream) : launch_fwd_t<BF16, 64, false>(a, stream);
   return D == 128 ? launch_fwd_t<F16, 128, false>(a, stream) : launch_fwd_t<F16, 64, false>(a, stream);
+}
+
+hipError_t launch_fwd_dropout(const FwdArgs& a, int D, int dtype, hipStream_t stream) {
+  if (dtype == 1)
+    return D == 128 ? launch_fwd_t<BF16, 128, false, true>(a, stream) : launch_fwd_t<BF16, 64, false, true>(a, stream);
+  return D == 128 ? launch_fwd_t<F16, 128, false, true>(a, stream) : launch_fwd_t<F16, 64, false, true>(a, stream);
 }
 
 hipError_t launch_fwd_paged(const FwdArgs& a, int D, int dtype, hipStream_t stream) {

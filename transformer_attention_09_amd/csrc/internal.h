@@ -25,6 +25,12 @@ struct FwdArgs {
   const int32_t* block_table;
   const int32_t* ctx_lens;
   int max_blocks_per_seq, num_blocks;
+  // Dropout on the probabilities (attn_fwd_dropout): element (b, h, i, j) is
+  // kept iff word j%4 of Philox4x32-10 at counter (j/4, i, b*Hq+h,
+  // drop_offset) under key (seed_lo, seed_hi) is >= drop_thr; kept ones
+  // are scaled by drop_scale = 1/(1-p).  Unused by the other entry points.
+  uint32_t drop_thr, seed_lo, seed_hi, drop_offset;
+  float drop_scale;
 };
 
 // Paged decode.  The cache blocks of all sequences, taken in sequence order,
@@ -101,6 +107,7 @@ constexpr int kDecodeMaxStreams = 2048;
 constexpr int kDecodeWavesPerCU = 4;
 
 hipError_t launch_fwd(const FwdArgs& a, int D, int dtype, hipStream_t stream);
+hipError_t launch_fwd_dropout(const FwdArgs& a, int D, int dtype, hipStream_t stream);
 hipError_t launch_fwd_paged(const FwdArgs& a, int D, int dtype, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, int D, int dtype, hipStream_t stream);
 hipError_t launch_fwd_fp8(const F8Args& a, int D, hipStream_t stream);
