@@ -245,6 +245,27 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
              float scale, int causal, int window, int dtype,
              void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * attn_bwd_dropout - gradients of L = sum(dout * out) for the out of
+ * attn_fwd_dropout(q, k, v, ..., dropout_p, seed, offset) called with the
+ * same arguments (out and lse are that call's).
+ *
+ * The keep decisions are recomputed from (seed, offset) with the forward's
+ * counter, so no mask is stored.  With M = keep / (1 - dropout_p):
+ *   dv = (P * M)^T dout;  dS = P * (M * (dout v^T) - rowsum(dout * out));
+ *   dq = scale * dS k;  dk = scale * dS^T q
+ * (the row sum of dout * out equals sum_j P_ij M_ij (dout v^T)_ij, as without
+ * dropout).  Tensors, workspace, determinism, empty sizes and errors as
+ * attn_bwd; dropout_p outside [0, 1) is ATTN_ERR_SHAPE, and dropout_p = 0
+ * gives attn_bwd's result.
+ */
+int attn_bwd_dropout(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                     const float* lse, void* dq, void* dk, void* dv,
+                     int B, int Hq, int Hkv, int Lq, int Lk, int D,
+                     float scale, int causal, int window,
+                     float dropout_p, uint64_t seed, uint32_t offset, int dtype,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of workspace attn_bwd needs (a pure host function); 0 when B*Hq*Lq = 0
  * or the arguments are invalid. */
 size_t attn_bwd_workspace_size(int B, int Hq, int Lq);

@@ -279,3 +279,33 @@ def test_fwd_dropout_valid_args_without_gpu_report_device():
     assert _drop() == DEV
     assert _drop(p=0.0) == DEV
     assert _drop(p=0.99999994) == DEV  # the largest float below 1
+
+
+def _bwd_drop(**kw):
+    a = dict(q=P, k=P, v=P, out=P, dout=P, lse=P, dq=P, dk=P, dv=P, B=1, Hq=4, Hkv=2, Lq=16, Lk=16, D=64,
+             scale=0.125, causal=0, window=-1, p=0.1, seed=3, offset=0, dtype=1, ws=P, ws_bytes=1 << 20)
+    a.update(kw)
+    return ta.load_library().attn_bwd_dropout(a["q"], a["k"], a["v"], a["out"], a["dout"], a["lse"], a["dq"],
+                                              a["dk"], a["dv"], a["B"], a["Hq"], a["Hkv"], a["Lq"], a["Lk"],
+                                              a["D"], a["scale"], a["causal"], a["window"], a["p"], a["seed"],
+                                              a["offset"], a["dtype"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(dout=None), NULL), (dict(lse=None), NULL), (dict(dk=None), NULL),
+    (dict(B=-1), SHAPE), (dict(Hq=6, Hkv=4), SHAPE), (dict(scale=float("nan")), SHAPE),
+    (dict(p=1.0), SHAPE), (dict(p=-1e-7), SHAPE), (dict(p=float("nan")), SHAPE),
+    (dict(D=32), UNSUP), (dict(dtype=5), UNSUP),
+    (dict(dq=P + 8), ALIGN), (dict(lse=P + 2), ALIGN),
+    (dict(ws=None), WS), (dict(ws_bytes=16), WS), (dict(ws=P + 4), WS),
+    (dict(B=0), OK),
+])
+def test_bwd_dropout_validation(kw, code):
+    assert _bwd_drop(**kw) == code
+
+
+def test_bwd_dropout_valid_args_without_gpu_report_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: valid arguments would launch on the fake address")
+    assert _bwd_drop() == DEV

@@ -161,3 +161,143 @@ def test_dropout_empty_keys_and_rows(gpu_lib):
     assert torch.all(o0 == 0) and torch.all(torch.isneginf(l0))
     e, le = gpu_lib.attn_fwd_dropout(q[:, :0], k, v, 0.5, 1, 0)
     assert e.numel() == 0 and le.numel() == 0
+
+
+# ---------------------------------------------------------------- backward
+
+GTOL = {"fp16": 2e-3, "bf16": 1.6e-2}
+
+
+def _dout(shape, dtype, seed):
+    r = np.random.default_rng(seed)
+    return torch.from_numpy(r.standard_normal(size=shape, dtype=np.float32)).to(DTYPES[dtype])
+
+
+def run_bwd_drop(ta, q, k, v, do, p, seed, offset, scale, causal, window):
+    qd, kd, vd, dod = (t.to("cuda") for t in (q, k, v, do))
+    out, lse = ta.attn_fwd_dropout(qd, kd, vd, p, seed, offset, scale=scale, causal=causal, window=window)
+    grads = ta.attn_bwd_dropout(qd, kd, vd, out, dod, lse, p, seed, offset, scale=scale, causal=causal,
+                                window=window)
+    torch.cuda.synchronize()
+    return grads
+
+
+BWD_CASES = [
+    # B, Hq, Hkv, Lq, Lk, D, dtype, causal, window, p
+    (1, 2, 1, 128, 128, 64, "fp16", False, -1, 0.1),
+    (2, 4, 2, 200, 333, 128, "bf16", True, -1, 0.2),
+    (1, 4, 1, 300, 150, 64, "bf16", True, -1, 0.5),
+    (1, 2, 2, 257, 257, 128, "fp16", True, 64, 0.1),
+    (2, 6, 3, 100, 77, 64, "bf16", False, 20, 0.3),
+    (1, 3, 1, 1, 65, 64, "fp16", True, -1, 0.7),
+    (1, 2, 1, 70, 1, 128, "fp16", False, -1, 0.5),
+]
+
+
+@pytest.mark.parametrize("case", range(len(BWD_CASES)))
+def test_dropout_backward_cases(gpu_lib, case):
+    """Tolerance: the backward's per-dtype bound times max(1, max|ref|), and
+    times 1 / (1 - p), the factor dropout puts on the kept terms."""
+    B, Hq, Hkv, Lq, Lk, D, dtype, causal, window, p = BWD_CASES[case]
+    say(f"[case] dropout bwd {case}: B{B} Hq{Hq} Hkv{Hkv} Lq{Lq} Lk{Lk} D{D} {dtype} causal{causal} w{window} p{p}")
+    q, k, v = random_dense(B, Hq, Hkv, Lq, Lk, D, dtype, 1400 + case)
+    do = _dout(q.shape, dtype, 1500 + case)
+    scale = 1.0 / np.sqrt(D)
+    seed, offset = 31 + case, 7 * case
+    got = run_bwd_drop(gpu_lib, q, k, v, do, p, seed, offset, scale, causal, window)
+    ref = oracle.attention_dropout_backward(q, k, v, do, scale, causal, window, p, seed, offset)
+    msgs = []
+    for n, g, r in zip(("dq", "dk", "dv"), got, ref):
+        g = g.double().cpu().numpy()
+        assert not np.isnan(g).any(), f"{n}: NaN"
+        err = float(np.max(np.abs(g - r))) if g.size else 0.0
+        mag = max(1.0, float(np.max(np.abs(r)))) if r.size else 1.0
+        tol = GTOL[dtype] * mag / (1.0 - float(np.float32(p)))
+        msgs.append(f"{n} max-abs {err:.3e} (tol {tol:.2e})")
+        assert err <= tol, "; ".join(msgs)
+    say("  " + "; ".join(msgs))
+
+
+@pytest.mark.parametrize("D,dtype,p,Lq,Lk", [(64, "fp16", 0.3, 300, 300), (128, "bf16", 0.6, 257, 400)])
+def test_dropout_backward_keep_decisions(gpu_lib, D, dtype, p, Lq, Lk):
+    """Both backward kernels' keep decisions, element by element.
+
+    Keys, values and output gradients are one-hot, with a causal window of
+    D - 1 keys, so that each row sees D keys of distinct j mod D and each key
+    is seen by D rows of distinct i mod D:
+      * dout_i = e_{i mod D}:  dv[j, i mod D] = P_ij M_ij, nonzero iff kept
+        (the dK/dV kernel's decision);
+      * dout = 1, k_j = v_j = e_{j mod D}: dq[i, j mod D] = scale * dS_ij with
+        dS_ij = P_ij (M_ij - D_i), i.e. scale * P_ij (1/(1-p) - D_i) if kept and
+        -scale * P_ij D_i if dropped; the kernel's value is classified by the
+        nearer of the two (fp64 oracle values), which must give the oracle's
+        decision (the dQ kernel's decision).
+    """
+    B, H, W = 1, 2, D - 1
+    seed, offset = 0xC0FFEE, 17
+    say(f"[case] dropout bwd decisions D{D} {dtype} p{p} Lq{Lq} Lk{Lk}")
+    rng = np.random.default_rng(1600 + D)
+    q = torch.from_numpy(rng.standard_normal((B, Lq, H, D), dtype=np.float32)).to(DTYPES[dtype])
+    onehot_k = np.zeros((B, Lk, H, D), dtype=np.float32)
+    onehot_k[:, np.arange(Lk), :, np.arange(Lk) % D] = 1.0
+    kv = torch.from_numpy(onehot_k).to(DTYPES[dtype])
+    scale = 1.0 / np.sqrt(D)
+    ok = oracle.allowed_mask(Lq, Lk, True, W)
+    i_idx, j_idx = np.nonzero(ok)
+
+    # dK/dV kernel: dout_i = e_{i mod D}
+    do_a = np.zeros((B, Lq, H, D), dtype=np.float32)
+    do_a[:, np.arange(Lq), :, np.arange(Lq) % D] = 1.0
+    k_rand = torch.from_numpy(rng.standard_normal((B, Lk, H, D), dtype=np.float32)).to(DTYPES[dtype])
+    _, _, dv = run_bwd_drop(gpu_lib, q, k_rand, kv, torch.from_numpy(do_a).to(DTYPES[dtype]), p, seed, offset,
+                            scale, True, W)
+    dv = dv.float().cpu().numpy()
+    for h in range(H):
+        keep = oracle.dropout_keep(h, np.arange(Lq), Lk, p, seed, offset)
+        got = dv[0, j_idx, h, i_idx % D] > 0
+        bad = int(np.count_nonzero(got != keep[i_idx, j_idx]))
+        assert bad == 0, f"dK/dV kernel, head {h}: {bad} of {len(got)} decisions differ"
+
+    # dQ kernel: dout = 1, k = v = one-hot
+    do_b = torch.ones((B, Lq, H, D), dtype=DTYPES[dtype])
+    dq, _, _ = run_bwd_drop(gpu_lib, q, kv, kv, do_b, p, seed, offset, scale, True, W)
+    dq = dq.double().cpu().numpy()
+    Pm, _ = oracle.attention(q, kv, kv, scale, True, W)  # one-hot values: column j mod D of row i is P_ij
+    inv = 1.0 / (1.0 - float(np.float32(p)))
+    for h in range(H):
+        keep = oracle.dropout_keep(h, np.arange(Lq), Lk, p, seed, offset)
+        Pij = Pm[0, i_idx, h, j_idx % D]            # P_ij (values one-hot: column j mod D of row i)
+        Di = np.zeros(Lq)
+        np.add.at(Di, i_idx, Pij * np.where(keep[i_idx, j_idx], inv, 0.0))
+        hyp_keep = scale * Pij * (inv - Di[i_idx])
+        hyp_drop = -scale * Pij * Di[i_idx]
+        g = dq[0, i_idx, h, j_idx % D]
+        got = np.abs(g - hyp_keep) < np.abs(g - hyp_drop)
+        bad = int(np.count_nonzero(got != keep[i_idx, j_idx]))
+        assert bad == 0, f"dQ kernel, head {h}: {bad} of {len(got)} decisions differ"
+    say(f"  {H * len(i_idx)} decisions per kernel agree")
+
+
+def test_dropout_backward_zero_probability_is_attn_bwd_bitwise(gpu_lib):
+    q, k, v = (t.to("cuda") for t in random_dense(1, 4, 2, 190, 230, 128, "bf16", 1700))
+    do = _dout(q.shape, "bf16", 1701).to("cuda")
+    out, lse = gpu_lib.attn_fwd(q, k, v, causal=True)
+    a = gpu_lib.attn_bwd_dropout(q, k, v, out, do, lse, 0.0, 9, 9, causal=True)
+    b = gpu_lib.attn_bwd(q, k, v, out, do, lse, causal=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_dropout_backward_workload_std2048(gpu_lib):
+    cfg = CONFIGS["std2048"]
+    say("[case] dropout bwd workload std2048 p0.1")
+    q, k, v = dense_inputs(cfg)
+    do = _dout(q.shape, cfg.dtype, 1800)
+    got = run_bwd_drop(gpu_lib, q, k, v, do, 0.1, 5, 2, cfg.scale, cfg.causal, cfg.window)
+    ref = oracle.attention_dropout_backward(q, k, v, do, cfg.scale, cfg.causal, cfg.window, 0.1, 5, 2)
+    for n, g, r in zip(("dq", "dk", "dv"), got, ref):
+        err = float(np.max(np.abs(g.double().cpu().numpy() - r)))
+        tol = GTOL[cfg.dtype] * max(1.0, float(np.max(np.abs(r)))) / 0.9
+        say(f"  {n} max-abs {err:.3e} (tol {tol:.2e})")
+        assert err <= tol

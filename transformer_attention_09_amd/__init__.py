@@ -9,6 +9,7 @@ the C ABI declared in include/attn.h, with the same entry-point names:
     attn_decode_paged(q, k_cache, ...)      q [S,Hq,D], caches [N,16,Hkv,D]
     attn_fwd_paged(q, k_cache, ...)         q [B,Lq,Hq,D] over paged caches [N,16,Hkv,D]
     attn_bwd(q, k, v, out, dout, lse, ...)  gradients dq, dk, dv
+    attn_bwd_dropout(..., p, seed, ...)     gradients of attn_fwd_dropout's output
     attn_fwd_fp8(q, k, v, ...)              float8_e4m3fn inputs, bf16 output
     attn_bwd_workspace_size(B, Hq, Lq)
     attn_decode_paged_workspace_size(...)
@@ -42,7 +43,7 @@ STATUS = {
 }
 EXPORTED = ("attn_fwd", "attn_decode_paged", "attn_decode_paged_workspace_size", "attn_status_string",
             "attn_fwd_paged", "attn_bwd", "attn_bwd_workspace_size", "attn_fwd_fp8", "attn_hbm_read_probe",
-            "attn_fwd_dropout")
+            "attn_fwd_dropout", "attn_bwd_dropout")
 
 _lib = None
 _lock = threading.Lock()
@@ -89,6 +90,10 @@ def load_library() -> ctypes.CDLL:
             lib.attn_fwd_dropout.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32,
                                              f32, ctypes.c_uint64, ctypes.c_uint32, i32, vp]
             lib.attn_fwd_dropout.restype = i32
+            lib.attn_bwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                             f32, i32, i32, f32, ctypes.c_uint64, ctypes.c_uint32, i32,
+                                             vp, sz, vp]
+            lib.attn_bwd_dropout.restype = i32
             _lib = lib
     return _lib
 
@@ -325,10 +330,8 @@ def attn_bwd_workspace_size(B: int, Hq: int, Lq: int) -> int:
     return int(load_library().attn_bwd_workspace_size(B, Hq, Lq))
 
 
-def attn_bwd(q, k, v, out, dout, lse, dq=None, dk=None, dv=None, scale: Optional[float] = None,
-             causal: bool = False, window: int = -1, workspace=None, stream=None):
-    """Gradients (dq, dk, dv) of sum(dout * out) for out, lse = attn_fwd(q, k, v, ...)
-    called with the same scale, causal and window."""
+def _bwd_tensors(q, k, v, out, dout, lse, dq, dk, dv, scale, workspace):
+    """Check the backward's tensors; allocate gradients and workspace if not given."""
     import torch
 
     for n, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout), ("lse", lse)):
@@ -355,12 +358,37 @@ def attn_bwd(q, k, v, out, dout, lse, dq=None, dk=None, dv=None, scale: Optional
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    return dq, dk, dv, (B, Hq, Hkv, Lq, Lk, D), float(scale), ws_ptr, ws_bytes
+
+
+def attn_bwd(q, k, v, out, dout, lse, dq=None, dk=None, dv=None, scale: Optional[float] = None,
+             causal: bool = False, window: int = -1, workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of sum(dout * out) for out, lse = attn_fwd(q, k, v, ...)
+    called with the same scale, causal and window."""
+    dq, dk, dv, dims, scale, ws_ptr, ws_bytes = _bwd_tensors(q, k, v, out, dout, lse, dq, dk, dv, scale, workspace)
     st = load_library().attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
                                  lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                                 B, Hq, Hkv, Lq, Lk, D, float(scale), int(bool(causal)), int(window),
+                                 *dims, scale, int(bool(causal)), int(window),
                                  _dtype_code(q), ws_ptr, ws_bytes, _stream_handle(stream))
     if st != 0:
         raise AttnError(st, "attn_bwd")
+    return dq, dk, dv
+
+
+def attn_bwd_dropout(q, k, v, out, dout, lse, dropout_p: float, seed: int, offset: int = 0, dq=None, dk=None,
+                     dv=None, scale: Optional[float] = None, causal: bool = False, window: int = -1,
+                     workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of sum(dout * out) for out, lse =
+    attn_fwd_dropout(q, k, v, dropout_p, seed, offset, ...) called with the same
+    arguments; the keep decisions are recomputed from (seed, offset)."""
+    dq, dk, dv, dims, scale, ws_ptr, ws_bytes = _bwd_tensors(q, k, v, out, dout, lse, dq, dk, dv, scale, workspace)
+    st = load_library().attn_bwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                         dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                         dv.data_ptr(), *dims, scale, int(bool(causal)), int(window),
+                                         float(dropout_p), int(seed) & (2 ** 64 - 1), int(offset) & 0xFFFFFFFF,
+                                         _dtype_code(q), ws_ptr, ws_bytes, _stream_handle(stream))
+    if st != 0:
+        raise AttnError(st, "attn_bwd_dropout")
     return dq, dk, dv
 
 

@@ -225,17 +225,22 @@ ATTN_API size_t attn_bwd_workspace_size(int B, int Hq, int Lq) {
   return ((n * 4 + 15) & ~(size_t)15) * 2;  // D, then the base-2 lse, each 16-byte aligned
 }
 
-ATTN_API int attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
-                      const float* lse, void* dq, void* dk, void* dv,
-                      int B, int Hq, int Hkv, int Lq, int Lk, int D,
-                      float scale, int causal, int window, int dtype,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+// Validation and launch shared by attn_bwd and attn_bwd_dropout.
+int bwd_common(const void* q, const void* k, const void* v, const void* out, const void* dout,
+               const float* lse, void* dq, void* dk, void* dv,
+               int B, int Hq, int Hkv, int Lq, int Lk, int D,
+               float scale, int causal, int window, int dtype,
+               void* workspace, size_t workspace_bytes, void* stream,
+               bool drop, float dropout_p, uint64_t seed, uint32_t offset) {
   if (B < 0 || Lq < 0 || Lk < 0 || Hq <= 0 || Hkv <= 0) return ATTN_ERR_SHAPE;
   const bool q_empty = (B == 0 || Lq == 0), kv_empty = (B == 0 || Lk == 0);
   if (!q_empty && (!q || !out || !dout || !lse || !dq)) return ATTN_ERR_NULL;
   if (!kv_empty && (!k || !v || !dk || !dv)) return ATTN_ERR_NULL;
   if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
   if (!std::isfinite(scale)) return ATTN_ERR_SHAPE;
+  if (drop && !(dropout_p >= 0.f && dropout_p < 1.f)) return ATTN_ERR_SHAPE;  // NaN fails too
   if (!supported_d(D) || !supported_dtype(dtype)) return ATTN_ERR_UNSUPPORTED;
   if (!prod_ok(B, Lq, Hq, D) || !prod_ok(B, Lk, Hkv, D)) return ATTN_ERR_SHAPE;
   const long long n_qblocks = ((long long)Lq + attn::kPrefillBlockM - 1) / attn::kPrefillBlockM;
@@ -262,8 +267,36 @@ ATTN_API int attn_bwd(const void* q, const void* k, const void* v, const void* o
   a.scale = scale;
   a.scale_log2 = scale * attn::kLog2e;
   a.n_qblocks = (int)n_qblocks;
-  hipError_t e = attn::launch_bwd(a, D, dtype, (hipStream_t)stream);
+  // the forward's threshold and scale (attn_fwd_dropout)
+  a.drop_thr = drop ? (uint32_t)std::floor((double)dropout_p * 4294967296.0) : 0u;
+  a.drop_scale = drop ? (float)(1.0 / (1.0 - (double)dropout_p)) : 1.f;
+  a.seed_lo = (uint32_t)seed;
+  a.seed_hi = (uint32_t)(seed >> 32);
+  a.drop_offset = offset;
+  hipError_t e = drop ? attn::launch_bwd_dropout(a, D, dtype, (hipStream_t)stream)
+                      : attn::launch_bwd(a, D, dtype, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // namespace
+
+ATTN_API int attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                      const float* lse, void* dq, void* dk, void* dv,
+                      int B, int Hq, int Hkv, int Lq, int Lk, int D,
+                      float scale, int causal, int window, int dtype,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_common(q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Lq, Lk, D, scale, causal, window, dtype,
+                    workspace, workspace_bytes, stream, false, 0.f, 0u, 0u);
+}
+
+ATTN_API int attn_bwd_dropout(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                              const float* lse, void* dq, void* dk, void* dv,
+                              int B, int Hq, int Hkv, int Lq, int Lk, int D,
+                              float scale, int causal, int window,
+                              float dropout_p, uint64_t seed, uint32_t offset, int dtype,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_common(q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Lq, Lk, D, scale, causal, window, dtype,
+                    workspace, workspace_bytes, stream, true, dropout_p, seed, offset);
 }
 
 // Workspace slots of one decode launch: one per (range, sequence) pair that

@@ -28,6 +28,16 @@
 //                    dO in registers, dQ^T += K^T dS^T with K^T read transposed.
 // All MFMAs are v_mfma_f32_32x32x16 on 16-bit operands (P and dS are rounded
 // to the input type), accumulating in fp32.
+//
+// With dropout (the DROP instances) the forward computed O = (P * M) V with
+// M = keep / (1 - p); then dV = (P * M)^T dO and dS = P * (M * dP - D), where
+// D_i = sum_d dO_id O_id still equals sum_j P_ij M_ij dP_ij.  Both kernels
+// recompute the keep decisions with the forward's Philox counter
+// (j/4, i, b*Hq + h, offset): one call gives a row's four keys 4c..4c+3.  The
+// dQ kernel holds a row per lane and four consecutive keys per register
+// group, as the forward does; the dK/dV kernel holds a key per lane, so the
+// four lanes of a quad (four consecutive keys) each draw one row's call and
+// trade words with a 4x4 quad transpose.
 #include <hip/hip_runtime.h>
 
 #include "common.h"
@@ -92,7 +102,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------------ dK, dV
 
-template <typename TT, int D>
+template <typename TT, int D, bool DROP>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   using C = BwdCfg<D>;
   using E = typename TT::elem;
@@ -219,6 +229,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
     const float* ls = P ? lt1 : lt0;
     const float* ds = P ? dt1 : dt0;
     const int i0 = (qt_lo + it % nq) * C::BQ;
+    const uint32_t drop_bh = (uint32_t)(b * a.Hq + g * a.group + it / nq);
+    if constexpr (DROP) {
+      // With the draws below the loop is short of registers: make the LDS
+      // offsets opaque here so that their sums with the buffer bases are
+      // formed in the loop instead of being hoisted (and spilled) outside it.
+#pragma unroll
+      for (int s2 = 0; s2 < C::DSTEPS; ++s2) asm volatile("" : "+v"(noff[s2]));
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) asm volatile("" : "+v"(toff[dt]));
+    }
 
     // This wave's 32-row block rb = rh: S = Q K^T and dP = dO V^T (32 rows x
     // 32 keys), then P = exp2(S * scale * log2(e) - lse2) and dS = P (dP - D),
@@ -230,6 +250,25 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
     const int key = kw0 + l32;
     {
       const int rb = rh;
+      // Dropout: bit r of kbits keeps the element of accumulator register r
+      // (row 8*(r/4) + 4*hh + r%4 of the block, this lane's key).  Lane q of a
+      // quad draws the call of row 8*(r/4) + 4*hh + q for the quad's four
+      // keys; the transpose hands each lane its key's word of the four rows.
+      // Drawn before the products, while few registers are live.
+      uint32_t kbits = 0u;
+      if constexpr (DROP) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          uint32_t row = (uint32_t)(i0 + rb * 32 + 8 * r4 + 4 * hh + (l32 & 3));
+          uint32_t c0 = (uint32_t)(key >> 2), k0 = a.seed_lo, k1 = a.seed_hi;
+          asm volatile("" : "+v"(row), "+v"(c0), "+s"(k0), "+s"(k1));
+          const uint4 r = philox4x32_10(make_uint4(c0, row, drop_bh, a.drop_offset), k0, k1);
+          uint32_t w[4] = {r.x, r.y, r.z, r.w};
+          quad_transpose(w, l32 & 3);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) kbits |= (w[c] >= a.drop_thr ? 1u : 0u) << (4 * r4 + c);
+        }
+      }
       f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
       for (int s = 0; s < C::DSTEPS; ++s) {
@@ -252,7 +291,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
             const int r = 8 * h2 + e;
             const float lv = e < 4 ? lA[e] : lB[e - 4], dv = e < 4 ? dA[e] : dB[e - 4];
             pv[e] = fast_exp2(__builtin_fmaf(sacc[r], sl2, -lv));
-            sv[e] = pv[e] * (pacc[r] - dv);
+            if constexpr (DROP) {
+              const bool kp = (kbits >> r) & 1u;
+              sv[e] = pv[e] * ((kp ? pacc[r] * a.drop_scale : 0.f) - dv);
+              pv[e] = kp ? pv[e] * a.drop_scale : 0.f;
+            } else {
+              sv[e] = pv[e] * (pacc[r] - dv);
+            }
           }
         } else {
           asm volatile("" ::: "memory");  // a real branch: edge tiles are rare
@@ -266,7 +311,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
                              ((W < 0) | a.causal | (rel <= W));
             const float x = __builtin_fmaf(sacc[r], sl2, -lv);
             pv[e] = fast_exp2(vis ? x : -INFINITY);
-            sv[e] = pv[e] * (pacc[r] - dv);
+            if constexpr (DROP) {
+              const bool kp = (kbits >> r) & 1u;
+              sv[e] = pv[e] * ((kp ? pacc[r] * a.drop_scale : 0.f) - dv);
+              pv[e] = kp ? pv[e] * a.drop_scale : 0.f;
+            } else {
+              sv[e] = pv[e] * (pacc[r] - dv);
+            }
           }
         }
         const V8 bp = __builtin_bit_cast(V8, make_uint4(pack2<TT>(pv[0], pv[1]), pack2<TT>(pv[2], pv[3]),
@@ -345,7 +396,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------------ dQ
 
-template <typename TT, int D>
+template <typename TT, int D, bool DROP>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   using C = BwdCfg<D>;
   using E = typename TT::elem;
@@ -379,6 +430,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const int t_lo = j_lo / C::BN;
   const int t_hi = (j_hi >= j_lo) ? j_hi / C::BN + 1 : t_lo;
   const int qi = q0 + wave * 32 + l32;
+  const uint32_t drop_bh = (uint32_t)bh;  // b * Hq + hq
   int jlo_row = 0, jhi_row = a.Lk - 1;
   if (a.causal) jhi_row = min(jhi_row, qi + off);
   if (W >= 0) {
@@ -475,6 +527,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
                       (W < 0 || jt >= wr_hi + off - W) && (W < 0 || a.causal || jt + C::BN - 1 <= wr_lo + off + W) &&
                       (wr_lo + 31 < a.Lq);
     uint32_t pw[4][4];
+    // Dropout: bit 16*kh + r keeps register r of half kh; registers 4g'..4g'+3
+    // of half kh are the words of the call with counter word 0 = 16*t + 2*(4*kh + g') + hh.
+    uint32_t kbits = 0u;
+    if constexpr (DROP) {
+      uint32_t c0 = (uint32_t)(16 * t + hh), row = (uint32_t)qi, k0 = a.seed_lo, k1 = a.seed_hi;
+      asm volatile("" : "+v"(c0), "+v"(row), "+s"(k0), "+s"(k1));
+#pragma unroll
+      for (int g4 = 0; g4 < 8; ++g4) {
+        const uint4 r = philox4x32_10(make_uint4(c0 + 2 * g4, row, drop_bh, a.drop_offset), k0, k1);
+        const uint32_t th = a.drop_thr;
+        kbits |= ((r.x >= th ? 1u : 0u) | (r.y >= th ? 2u : 0u) | (r.z >= th ? 4u : 0u) | (r.w >= th ? 8u : 0u))
+                 << (4 * g4);
+      }
+    }
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
       float sv[16];
@@ -486,7 +552,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
           x = (j >= jlo_row && j <= jhi_row) ? x : -INFINITY;
         }
         const float p = fast_exp2(x);
-        sv[r] = p * (pt[kh][r] - dvv);
+        if constexpr (DROP)
+          sv[r] = p * (((kbits >> (16 * kh + r)) & 1u ? pt[kh][r] * a.drop_scale : 0.f) - dvv);
+        else
+          sv[r] = p * (pt[kh][r] - dvv);
       }
 #pragma unroll
       for (int m = 0; m < 8; ++m) pw[2 * kh + (m >> 2)][m & 3] = pack2<TT>(sv[2 * m], sv[2 * m + 1]);
@@ -530,7 +599,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   }
 }
 
-template <typename TT, int D>
+template <typename TT, int D, bool DROP = false>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   using C = BwdCfg<D>;
   const long long rows = (long long)a.B * a.Lq * a.Hq;
@@ -543,13 +612,13 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   }
   if (a.Lk > 0) {
     const long long kblocks = (long long)((a.Lk + C::BK - 1) / C::BK) * a.B * a.Hkv;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<TT, D>), dim3((unsigned)kblocks), dim3(512), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<TT, D, DROP>), dim3((unsigned)kblocks), dim3(512), 0, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const long long qblocks = (long long)a.n_qblocks * a.B * a.Hq;
   if (qblocks > 0) {
-    hipLaunchKernelGGL((bwd_dq_kernel<TT, D>), dim3((unsigned)qblocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<TT, D, DROP>), dim3((unsigned)qblocks), dim3(256), 0, stream, a);
     e = hipGetLastError();
   }
   return e;
@@ -558,6 +627,12 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
 hipError_t launch_bwd(const BwdArgs& a, int D, int dtype, hipStream_t stream) {
   if (dtype == 1) return D == 128 ? launch_bwd_t<BF16, 128>(a, stream) : launch_bwd_t<BF16, 64>(a, stream);
   return D == 128 ? launch_bwd_t<F16, 128>(a, stream) : launch_bwd_t<F16, 64>(a, stream);
+}
+
+hipError_t launch_bwd_dropout(const BwdArgs& a, int D, int dtype, hipStream_t stream) {
+  if (dtype == 1)
+    return D == 128 ? launch_bwd_t<BF16, 128, true>(a, stream) : launch_bwd_t<BF16, 64, true>(a, stream);
+  return D == 128 ? launch_bwd_t<F16, 128, true>(a, stream) : launch_bwd_t<F16, 64, true>(a, stream);
 }
 
 }  // namespace attn

@@ -277,6 +277,27 @@ __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1
   return c;
 }
 
+// 4x4 transpose inside each quad of lanes: lane q (q = lane % 4) holds row q
+// of a 4x4 matrix in x[0..3] and ends with column q (x[c] = row c, column q).
+// Two exchange stages across lane bits 0 and 1 (DPP quad permutations): at
+// stage b, the elements whose index differs from the lane in bit b trade
+// places with the partner lane's element of the mirrored index.
+__device__ __forceinline__ void quad_transpose(uint32_t (&x)[4], int q) {
+  constexpr int kSwap1 = 1 | (0 << 2) | (3 << 4) | (2 << 6);  // quad_perm [1,0,3,2]
+  constexpr int kSwap2 = 2 | (3 << 2) | (0 << 4) | (1 << 6);  // quad_perm [2,3,0,1]
+  const bool odd = q & 1, hi = q & 2;
+#pragma unroll
+  for (int e = 0; e < 4; e += 2) {  // pairs (0,1), (2,3)
+    const uint32_t r = (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? x[e] : x[e + 1]), kSwap1, 0xF, 0xF, false);
+    if (odd) x[e] = r; else x[e + 1] = r;
+  }
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {  // pairs (0,2), (1,3)
+    const uint32_t r = (uint32_t)__builtin_amdgcn_mov_dpp((int)(hi ? x[e] : x[e + 2]), kSwap2, 0xF, 0xF, false);
+    if (hi) x[e] = r; else x[e + 2] = r;
+  }
+}
+
 // f(std::integral_constant<int, i>) for i = 0..N-1, expanded at compile time,
 // so that per-iteration indices (register array slots, schedule positions)
 // are constants.

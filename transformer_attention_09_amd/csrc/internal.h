@@ -77,6 +77,10 @@ struct BwdArgs {
   float scale;
   float scale_log2;
   int n_qblocks;
+  // Dropout (attn_bwd_dropout): the forward's keep decisions, recomputed
+  // with the same Philox counter, key and threshold as FwdArgs.
+  uint32_t drop_thr, seed_lo, seed_hi, drop_offset;
+  float drop_scale;
 };
 
 // FP8 forward: q, k, v e4m3 (OCP float8_e4m3fn), out bf16; scale_log2 holds
@@ -110,6 +114,7 @@ hipError_t launch_fwd(const FwdArgs& a, int D, int dtype, hipStream_t stream);
 hipError_t launch_fwd_dropout(const FwdArgs& a, int D, int dtype, hipStream_t stream);
 hipError_t launch_fwd_paged(const FwdArgs& a, int D, int dtype, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, int D, int dtype, hipStream_t stream);
+hipError_t launch_bwd_dropout(const BwdArgs& a, int D, int dtype, hipStream_t stream);
 hipError_t launch_fwd_fp8(const F8Args& a, int D, hipStream_t stream);
 hipError_t launch_decode(const DecArgs& a, int D, int dtype, hipStream_t stream);
 hipError_t launch_hbm_read(const void* p, size_t bytes, unsigned* sink, int cus, hipStream_t stream);
