@@ -494,6 +494,27 @@ def main():
             detail["bwd_" + name] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(fl / ms / 1e9, 1),
                                      "frac_mfma": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
             log(f"detail bwd_{name}: {detail['bwd_' + name]}")
+            if name == "gqa8k_causal":
+                # the same backward with dropout p = 0.1 (decisions recomputed in both kernels)
+                bo, bl = ta.attn_fwd_dropout(bq, bk, bv, 0.1, 1234, 0, scale=cfg.scale, causal=cfg.causal,
+                                             stream=stream)
+
+                def backward_drop():
+                    ta.attn_bwd_dropout(bq, bk, bv, bo, bdo, bl, 0.1, 1234, 0, dq=bdq, dk=bdk, dv=bdv,
+                                        scale=cfg.scale, causal=cfg.causal, workspace=bws, stream=stream)
+
+                for _ in range(2):
+                    backward_drop()
+                e0.record(stream)
+                for _ in range(5):
+                    backward_drop()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ms_d = e0.elapsed_time(e1) / 5
+                detail["bwd_dropout_" + name] = {"us": round(ms_d * 1e3, 2), "TFLOP/s": round(fl / ms_d / 1e9, 1),
+                                                 "frac_mfma": round(fl / ms_d / 1e9 / PEAK_BF16_TFLOPS, 4),
+                                                 "time_vs_plain": round(ms_d / ms, 3)}
+                log(f"detail bwd_dropout_{name}: {detail['bwd_dropout_' + name]}")
             del bq, bk, bv, bo, bl, bdo, bdq, bdk, bdv, bws
 
         # paged prefill: 512 new tokens per sequence over paged contexts
