@@ -105,3 +105,14 @@ def test_fp8_deterministic_bitwise(gpu_lib):
     a = run_fp8(gpu_lib, q, k, v, cfg.scale, True, -1)
     b = run_fp8(gpu_lib, q, k, v, cfg.scale, True, -1)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("scale", [-0.09, 0.0])
+def test_fp8_negative_and_zero_scale(gpu_lib, scale):
+    # the kernel moves a negative scale into Q (sign flip of every e4m3 byte)
+    # and zeroes Q for a zero scale (uniform attention over the visible keys)
+    cfg = DenseConfig("fp8_sign", 1, 4, 2, 150, 190, 128, "fp8", True, -1, 970)
+    q, k, v = dense_inputs(cfg)
+    say(f"[case] fp8 scale {scale}")
+    out, lse = run_fp8(gpu_lib, q, k, v, scale, True, -1, 1.5, 1.0, 0.5)
+    check_fp8(f"fp8 scale {scale}", out, lse, q, k, v, scale, True, -1, 1.5, 1.0, 0.5)

@@ -46,7 +46,7 @@ struct F8Cfg {
 // Chunk swizzle inside a row: 16 consecutive rows of a row read, and the 8
 // rows x 16 bytes of a transposed read, fall on distinct LDS banks.
 template <int D>
-__device__ __forceinline__ int f8swz(int r) {
+__device__ __forceinline__ constexpr int f8swz(int r) {
   if constexpr (D == 128) return (r >> 1) & 7;
   else return (r >> 2) & 3;
 }
@@ -102,7 +102,15 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(F8Args a) {
   }
   const int wr_lo = q0 + wave * 32, wr_hi = min(wr_lo + 31, a.Lq - 1);
 
-  // Q operand (B of S^T): row qi, head-dim bytes 64*s + 32*hh .. +31.
+  // Q operand (B of S^T): row qi, head-dim bytes 64*s + 32*hh .. +31.  The
+  // kernel keeps the base-2 scale positive, so that the row maximum can be
+  // taken on the raw scores and each probability is one FMA and one exp2: a
+  // negative scale moves into Q (an exact sign flip of every e4m3 byte) and
+  // a zero scale zeroes Q.
+  float sl2 = a.scale_log2;
+  uint32_t qsign = 0u, qkeep = 0xffffffffu;
+  if (sl2 < 0.f) { qsign = 0x80808080u; sl2 = -sl2; }
+  if (sl2 == 0.f) { qkeep = 0u; sl2 = 1.f; }
   i32x8 qf[C::KS];
   {
     const size_t base = (((size_t)b * a.Lq + q0) * a.Hq + hq) * D;
@@ -112,27 +120,27 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(F8Args a) {
 #pragma unroll
     for (int s = 0; s < C::KS; ++s) {
       const uint4 lo = buf_load16(rq, o + 64 * s), hi = buf_load16(rq, o + 64 * s + 16);
-      qf[s] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      qf[s] = i32x8{(int)((lo.x ^ qsign) & qkeep), (int)((lo.y ^ qsign) & qkeep), (int)((lo.z ^ qsign) & qkeep),
+                    (int)((lo.w ^ qsign) & qkeep), (int)((hi.x ^ qsign) & qkeep), (int)((hi.y ^ qsign) & qkeep),
+                    (int)((hi.z ^ qsign) & qkeep), (int)((hi.w ^ qsign) & qkeep)};
     }
   }
 
   // LDS offsets.  K row read: row l32 (+32 per key half), chunks 4s+2hh, +1.
-  int koff[C::KS][2];
-#pragma unroll
-  for (int s = 0; s < C::KS; ++s)
-#pragma unroll
-    for (int u = 0; u < 2; ++u) koff[s][u] = l32 * D + (((4 * s + 2 * hh + u) ^ f8swz<D>(l32)) << 4);
+  // The swizzle only permutes the chunk bits (4..log2(D)-1) of an offset, so
+  // chunk c ^ x of a row is the row's chunk-0 offset with (c << 4) XORed in:
+  // one base register per read kind, the rest folded into XOR immediates and
+  // the LDS instructions' offset fields.
+  const int kbase = l32 * D + (((2 * hh) ^ f8swz<D>(l32)) << 4);
+  auto koff = [&](int s, int u) { return kbase ^ ((4 * s + u) << 4); };
   // V^T transposed read j of head-dim tile dt: rows 16j + 8hh + j16/2,
-  // logical columns 32*dt + 16*(grp&1) + 8*(j16&1) .. +7.
-  int voff[C::DT][4];
-#pragma unroll
-  for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int rho = 16 * j + 8 * hh + (j16 >> 1);
-      const int col = 32 * dt + 16 * (grp & 1) + 8 * (j16 & 1);
-      voff[dt][j] = rho * D + ((((col >> 4) ^ f8swz<D>(rho)) << 4) | (col & 15));
-    }
+  // logical columns 32*dt + 16*(grp&1) + 8*(j16&1) .. +7.  The swizzle of
+  // rows 16j + c does not depend on j (it uses bits 1-3 of the row at D=128
+  // and 2-3 at D=64), so read j is read 0 plus 16*j rows.
+  static_assert(f8swz<D>(16) == f8swz<D>(0), "the V swizzle has period 16 rows");
+  const int vrow = 8 * hh + (j16 >> 1);
+  const int vbase = vrow * D + ((((16 * (grp & 1)) >> 4) ^ f8swz<D>(vrow)) << 4) + 8 * (j16 & 1);
+  auto voff = [&](int dt, int j) { return (vbase ^ ((2 * dt) << 4)) + 16 * j * D; };
 
   // Direct-to-LDS staging: lane -> LDS row (wave*IPW + i)*RPI + lane/CPR,
   // physical chunk lane%CPR, which holds logical chunk (lane%CPR) ^ swizzle.
@@ -167,7 +175,6 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(F8Args a) {
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt) oacc[dt] = f32x16{};
   float m_ref = -INFINITY, l_run = 0.f;
-  const float sl2 = a.scale_log2;
 
   auto body = [&](int t, auto par) {
     constexpr int P = decltype(par)::value;
@@ -181,8 +188,8 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(F8Args a) {
       st[kh] = f32x16{};
 #pragma unroll
       for (int s = 0; s < C::KS; ++s) {
-        const uint4 lo = *(const uint4*)(ks + koff[s][0] + kh * 32 * D);
-        const uint4 hi = *(const uint4*)(ks + koff[s][1] + kh * 32 * D);
+        const uint4 lo = *(const uint4*)(ks + koff(s, 0) + kh * 32 * D);
+        const uint4 hi = *(const uint4*)(ks + koff(s, 1) + kh * 32 * D);
         const i32x8 ka = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         st[kh] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qf[s], st[kh], 0, 0, 0, 0, 0, 0);
       }
@@ -192,21 +199,29 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(F8Args a) {
     const bool full = (jt + C::BN <= a.Lk) && (!a.causal || jt + C::BN - 1 <= wr_lo + off) &&
                       (W < 0 || jt >= wr_hi + off - W) && (W < 0 || a.causal || jt + C::BN - 1 <= wr_lo + off + W) &&
                       (wr_lo + 31 < a.Lq);
+    // Raw scores (sl2 > 0 keeps their order); edge tiles are masked in one
+    // rare branch, not per element.
+    if (!full) {
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = jt + 32 * kh + 8 * (r >> 2) + 4 * hh + (r & 3);
+          st[kh][r] = (j >= jlo_row && j <= jhi_row) ? st[kh][r] : -INFINITY;
+        }
+    }
     float x[32];
-    float mx = -INFINITY;
+    float mx_a = -INFINITY, mx_b = -INFINITY;
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float v = st[kh][r] * sl2;
-        if (!full) {
-          const int j = jt + 32 * kh + 8 * (r >> 2) + 4 * hh + (r & 3);
-          v = (j >= jlo_row && j <= jhi_row) ? v : -INFINITY;
-        }
-        x[16 * kh + r] = v;
-        mx = fmaxf(mx, v);
+        x[16 * kh + r] = st[kh][r];
+        if (r & 1) mx_b = fmaxf(mx_b, st[kh][r]);
+        else mx_a = fmaxf(mx_a, st[kh][r]);
       }
-    mx = max_xor32(mx);
+    const float mx = max_xor32(fmaxf(mx_a, mx_b)) * sl2;  // -inf stays -inf
     // Move the exponent base only when this row's maximum passes it by > 8,
     // and then to 8 below the maximum (probabilities stay in (0, 2^8]).
     const bool need = mx > m_ref + 8.f;
@@ -225,8 +240,10 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(F8Args a) {
     float rs = 0.f;
 #pragma unroll
     for (int w4 = 0; w4 < 8; ++w4) {
-      const float p0 = fast_exp2(x[4 * w4] + nb), p1 = fast_exp2(x[4 * w4 + 1] + nb);
-      const float p2 = fast_exp2(x[4 * w4 + 2] + nb), p3 = fast_exp2(x[4 * w4 + 3] + nb);
+      const float p0 = fast_exp2(__builtin_fmaf(x[4 * w4], sl2, nb));
+      const float p1 = fast_exp2(__builtin_fmaf(x[4 * w4 + 1], sl2, nb));
+      const float p2 = fast_exp2(__builtin_fmaf(x[4 * w4 + 2], sl2, nb));
+      const float p3 = fast_exp2(__builtin_fmaf(x[4 * w4 + 3], sl2, nb));
       rs += (p0 + p1) + (p2 + p3);
       int w = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
       pk[w4] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, w, true);
@@ -236,10 +253,10 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(F8Args a) {
     // O^T += V^T P^T: one MFMA per head-dim tile covers the 64 keys.
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) {
-      const i32x8 va = cat8(__builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS_PTR(i32x2, vs + voff[dt][0])),
-                            __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS_PTR(i32x2, vs + voff[dt][1])),
-                            __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS_PTR(i32x2, vs + voff[dt][2])),
-                            __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS_PTR(i32x2, vs + voff[dt][3])));
+      const i32x8 va = cat8(__builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS_PTR(i32x2, vs + voff(dt, 0))),
+                            __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS_PTR(i32x2, vs + voff(dt, 1))),
+                            __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS_PTR(i32x2, vs + voff(dt, 2))),
+                            __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS_PTR(i32x2, vs + voff(dt, 3))));
       oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, oacc[dt], 0, 0, 0, 0, 0, 0);
     }
     wait_vmem();
