@@ -209,11 +209,20 @@ def read_ceiling(ta, torch, dev, stream, nbytes=2 << 30, reps=5):
     return nbytes / (ms * 1e-3) / 1e9
 
 
+def under_profiler() -> bool:
+    """Is this process running under rocprofv3 (its tool library preloaded)?"""
+    return any(k.startswith("ROCPROF") for k in os.environ) or "rocprof" in os.environ.get("LD_PRELOAD", "")
+
+
 def sclk_under_load(run_batch):
     """Shader clock (MHz) reported by rocm-smi while a batch of forward launches
-    is running; None if the tool is not available."""
+    is running; None if the tool is not available.  Not sampled under a
+    profiler: its preloaded library would start the GPU in the child process
+    before rocm-smi's interpreter replaces it."""
     import re
     import subprocess
+    if under_profiler():
+        return None
     run_batch()
     try:
         r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=60)
