@@ -393,6 +393,10 @@ PREFILL_CASES = [
     (64, "bf16", 2, 2, 256, [1, 128, 300, 1024], False, 50),
     (128, "bf16", 12, 2, 1, [5, 4096, 16, 17], True, -1),
     (64, "fp16", 4, 4, 129, [129, 128, 0, 2000], True, 0),
+    # item counts around the kernel's 64-item longest-first ordering: exactly
+    # 64 (sequence, q-block) items, and 70 (the plain order)
+    (128, "fp16", 2, 1, 200, [int(x) for x in np.random.default_rng(77).integers(200, 900, 32)], True, -1),
+    (64, "bf16", 4, 2, 10, [int(x) for x in np.random.default_rng(78).integers(0, 300, 70)], True, -1),
 ]
 
 

@@ -126,26 +126,62 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       hj = r % a.group;
     }
   }
-  const int b = gid / a.Hkv, g = gid % a.Hkv;
+  int b = gid / a.Hkv;
+  const int g = gid % a.Hkv;
   const int hq = g * a.group + hj;
+  const int W = a.window;
+  // Key-tile range [t_lo, t_hi) of the q-block starting at row q0 over Lk keys.
+  auto tile_range = [&](int q0_, int Lk_, int& t_lo_, int& t_hi_) {
+    const int off_ = Lk_ - a.Lq;
+    const int row_hi = min(q0_ + C::BM, a.Lq) - 1;
+    int j_lo = 0, j_hi = Lk_ - 1;
+    if (a.causal) j_hi = min(j_hi, row_hi + off_);
+    if (W >= 0) {
+      j_lo = max(j_lo, q0_ + off_ - W);
+      if (!a.causal) j_hi = min(j_hi, row_hi + off_ + W);
+    }
+    t_lo_ = j_lo / C::BN;
+    t_hi_ = (j_hi >= j_lo) ? j_hi / C::BN + 1 : t_lo_;
+  };
+  auto ctx_len = [&](int bb) { return min(max(a.ctx_lens[bb], 0), a.max_blocks_per_seq * kPagedBlock); };
+  int qbr = qb_rank;
+  if constexpr (PAGED) {
+    // Paged contexts differ in length, so the (sequence, q-block) items
+    // differ in work.  With at most 64 items the work-groups take them
+    // longest first: item i = (q-block rank i / B, sequence i % B) goes to
+    // the work-groups of the item whose rank in descending tile count (ties
+    // by index) is i.  Every wave ranks the items in one pass, a lane each.
+    const int n_items = a.B * a.n_qblocks;
+    if (n_items <= 64) {
+      int w = -1;
+      if (lane < n_items) {
+        const int r = lane / a.B, qbl = a.causal ? (a.n_qblocks - 1 - r) : r;
+        int tl, th;
+        tile_range(qbl * C::BM, ctx_len(lane % a.B), tl, th);
+        w = th - tl;
+      }
+      int rank = 0;
+      for (int j = 0; j < n_items; ++j) {
+        const int wj = __builtin_amdgcn_readlane(w, j);
+        rank += (wj > w || (wj == w && j < lane)) ? 1 : 0;
+      }
+      const int it = qb_rank * a.B + b;
+      const unsigned long long hit = __ballot(lane < n_items && rank == it);
+      const int item = __builtin_amdgcn_readfirstlane(__builtin_ffsll((long long)hit) - 1);
+      qbr = item / a.B;
+      b = item % a.B;
+    }
+  }
   // Keys of batch row b: Lk of the dense layout, or the paged context length.
   int Lk = a.Lk;
-  if constexpr (PAGED) Lk = min(max(a.ctx_lens[b], 0), a.max_blocks_per_seq * kPagedBlock);
-  const int qb = a.causal ? (a.n_qblocks - 1 - qb_rank) : qb_rank;
+  if constexpr (PAGED) Lk = ctx_len(b);
+  const int qb = a.causal ? (a.n_qblocks - 1 - qbr) : qbr;
   const int q0 = qb * C::BM;
   const int off = Lk - a.Lq;  // bottom-right alignment of the causal diagonal
-  const int W = a.window;
 
   // ---- key-tile range of the whole work-group
-  const int row_hi = min(q0 + C::BM, a.Lq) - 1;
-  int j_lo = 0, j_hi = Lk - 1;
-  if (a.causal) j_hi = min(j_hi, row_hi + off);
-  if (W >= 0) {
-    j_lo = max(j_lo, q0 + off - W);
-    if (!a.causal) j_hi = min(j_hi, row_hi + off + W);
-  }
-  const int t_lo = j_lo / C::BN;
-  const int t_hi = (j_hi >= j_lo) ? j_hi / C::BN + 1 : t_lo;
+  int t_lo, t_hi;
+  tile_range(q0, Lk, t_lo, t_hi);
 
   // ---- this lane's query row and its Q operand (B of S^T = K Q^T).
   // The kernel keeps the base-2 scale positive: a negative scale is moved
