@@ -15,7 +15,9 @@ exact result needs only a small part of them:
   * a paged KV pool of more than 2 GiB whose sequences sit in its last blocks,
     random, with the oracle run on a compact copy of the blocks they use;
   * the backward of the windowed case: the oracle's gradients on the slice,
-    and exactly zero dk, dv for every key outside the window.
+    and exactly zero dk, dv for every key outside the window;
+  * the FP8 forward's windowed case over 2^24 + 4096 one-byte keys, within
+    that forward's derived bound.
 """
 import math
 import sys
@@ -161,3 +163,30 @@ def test_backward_window_past_2gib(gpu_lib):
         tol = TOL_BF16 * max(1.0, float(np.max(np.abs(r))))
         say(f"  {n} max-abs {err:.3e} (tol {tol:.2e})")
         assert err <= tol
+
+
+def test_fp8_window_past_2gib(gpu_lib):
+    # e4m3 keys are one byte per element: 2^24 + 4096 keys x 128 = 2.15 GB per K/V
+    Lk, Lq, Hq, Hkv, D, W = (1 << 24) + 4096, 64, 2, 1, 128, 200
+    say(f"[case] fp8 forward window {W} at the end of {Lk} keys")
+    s0 = Lk - Lq - W - 64
+    ks = randn((1, Lk - s0, Hkv, D), 51, torch.float32).to(torch.float8_e4m3fn)
+    vs = randn((1, Lk - s0, Hkv, D), 52, torch.float32).to(torch.float8_e4m3fn)
+    q = randn((1, Lq, Hq, D), 53, torch.float32).to(torch.float8_e4m3fn)
+    k = torch.zeros((1, Lk, Hkv, D), dtype=torch.float8_e4m3fn, device="cuda")
+    v = torch.zeros_like(k)
+    k[:, s0:] = ks.to("cuda")
+    v[:, s0:] = vs.to("cuda")
+    scale = 1.0 / math.sqrt(D)
+    out, lse = gpu_lib.attn_fwd_fp8(q.to("cuda"), k, v, scale=scale, causal=True, window=W)
+    torch.cuda.synchronize()
+    q64, k64, v64 = (t.double().numpy() for t in (q, ks, vs))
+    ref, rl = oracle.attention(q64, k64, v64, scale, True, W)
+    mag, _ = oracle.attention(q64, k64, np.abs(v64), scale, True, W)
+    # the FP8 forward's derived bound (e4m3 probabilities, bf16 output)
+    bound = 2.0 ** -4 * mag + 2.0 ** -8 * np.abs(ref) + 2e-3
+    o = out.double().cpu().numpy()
+    worst = float(np.max(np.abs(o - ref) / bound))
+    lerr = float(np.max(np.abs(lse.double().cpu().numpy() - rl)))
+    say(f"  worst err/bound {worst:.3f}, lse max-abs {lerr:.2e}")
+    assert worst <= 1.0 and lerr <= LSE_TOL
