@@ -71,29 +71,33 @@ def dropout_threshold(p: float) -> int:
     return int(math.floor(p32 * 2.0 ** 32))
 
 
-def dropout_keep(bh: int, rows, Lk: int, p: float, seed: int, offset: int) -> np.ndarray:
-    """Boolean [R, Lk]: is probability (row i, key j) of the (batch, head)
-    pair with linear index bh = b * Hq + h kept."""
+def dropout_keep(bh: int, rows, Lk: int, p: float, seed: int, offset: int, key0: int = 0) -> np.ndarray:
+    """Boolean [R, Lk]: is probability (row i, key key0 + c) of the (batch,
+    head) pair with linear index bh = b * Hq + h kept, for c = 0..Lk-1."""
     thr = dropout_threshold(p)
     i = np.asarray(rows, dtype=np.int64)
-    ngrp = (Lk + 3) // 4
-    ctr = np.empty((len(i), ngrp, 4), dtype=np.uint64)
-    ctr[..., 0] = np.arange(ngrp, dtype=np.uint64)[None, :]
+    g0, g1 = key0 // 4, (key0 + Lk + 3) // 4  # the 4-key groups that cover the keys
+    ctr = np.empty((len(i), g1 - g0, 4), dtype=np.uint64)
+    ctr[..., 0] = np.arange(g0, g1, dtype=np.uint64)[None, :]
     ctr[..., 1] = i.astype(np.uint64)[:, None]
     ctr[..., 2] = np.uint64(bh)
     ctr[..., 3] = np.uint64(offset & 0xFFFFFFFF)
     words = philox4x32(ctr, (seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF))
-    words = words.reshape(len(i), 4 * ngrp)[:, :Lk]
+    first = key0 - 4 * g0
+    words = words.reshape(len(i), 4 * (g1 - g0))[:, first:first + Lk]
     return words.astype(np.uint64) >= np.uint64(thr)
 
 
 def attention_dropout(q, k, v, scale: float, causal: bool = False, window: int = -1,
-                      p: float = 0.0, seed: int = 0, offset: int = 0, rows=None):
+                      p: float = 0.0, seed: int = 0, offset: int = 0, rows=None, key0: int = 0):
     """softmax(Q K^T * scale) with dropout on the probabilities, times V.
 
     out_i = sum_j P_ij * keep_ij * v_j / (1 - p), with P the row softmax over
     the visible keys and keep from dropout_keep; lse is the undropped one.
-    Shapes as in attention().  Returns (out, lse) in float64.
+    Shapes as in attention().  key0 numbers the given keys key0, key0 + 1, ...
+    in the keep decisions (a slice of a longer key sequence whose earlier keys
+    are invisible to every row); the masks are those of the slice.  Returns
+    (out, lse) in float64.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, Lq, Hq, D = q.shape
@@ -110,7 +114,7 @@ def attention_dropout(q, k, v, scale: float, causal: bool = False, window: int =
         for h in range(Hq):
             g = kv_head(h, Hq, Hkv)
             P, ls = row_softmax(scores(q[b, rr, h, :], k[b, :, g, :], sc), ok)
-            keep = dropout_keep(b * Hq + h, rr, Lk, p, seed, offset)
+            keep = dropout_keep(b * Hq + h, rr, Lk, p, seed, offset, key0)
             out[b, :, h, :] = (np.where(keep, P, 0.0) @ v[b, :, g, :]) * inv_keep
             lse[b, h, :] = ls
     return out, lse

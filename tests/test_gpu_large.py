@@ -17,7 +17,9 @@ exact result needs only a small part of them:
   * the backward of the windowed case: the oracle's gradients on the slice,
     and exactly zero dk, dv for every key outside the window;
   * the FP8 forward's windowed case over 2^24 + 4096 one-byte keys, within
-    that forward's derived bound.
+    that forward's derived bound;
+  * the dropout forward's windowed case, whose keep decisions use the keys'
+    absolute indices (the oracle numbers the slice's keys from its start).
 """
 import math
 import sys
@@ -190,3 +192,43 @@ def test_fp8_window_past_2gib(gpu_lib):
     lerr = float(np.max(np.abs(lse.double().cpu().numpy() - rl)))
     say(f"  worst err/bound {worst:.3f}, lse max-abs {lerr:.2e}")
     assert worst <= 1.0 and lerr <= LSE_TOL
+
+
+def test_dropout_window_past_2gib(gpu_lib):
+    # keep decisions at key indices past 12.5M (Philox counter word 0 past
+    # 3.1M) and K/V addresses past byte 2^31, bit for bit: with one-hot values
+    # v_j = e_(j mod D) and a causal window of D - 1 keys, output column
+    # j mod D of row i is P_ij * keep_ij / (1 - p), nonzero iff (i, j) was kept
+    Lq, Hq, Hkv, D, p = 96, 2, 1, 128, 0.2
+    W = D - 1
+    say(f"[case] dropout forward window {W} at the end of {LK} keys")
+    s0 = LK - Lq - W - 64
+    n = LK - s0
+    ks = randn((1, n, Hkv, D), 61)
+    onehot = torch.zeros((1, n, Hkv, D), dtype=torch.bfloat16)
+    j = torch.arange(s0, LK)
+    onehot[0, torch.arange(n), :, j % D] = 1.0
+    q = randn((1, Lq, Hq, D), 63)
+    k = torch.zeros((1, LK, Hkv, D), dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros_like(k)
+    k[:, s0:] = ks.to("cuda")
+    v[:, s0:] = onehot.to("cuda")
+    scale = 1.0 / math.sqrt(D)
+    seed, offset = 0xABCDEF0123, 5
+    out, lse = gpu_lib.attn_fwd_dropout(q.to("cuda"), k, v, p, seed, offset, scale=scale, causal=True, window=W)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy()
+    ok = oracle.allowed_mask(Lq, n, True, W)   # the slice's own masks (bottom-right, window)
+    i_idx, c_idx = np.nonzero(ok)
+    total = 0
+    for h in range(Hq):
+        keep = oracle.dropout_keep(h, np.arange(Lq), n, p, seed, offset, key0=s0)
+        got = o[0, i_idx, h, (s0 + c_idx) % D] > 0
+        bad = int(np.count_nonzero(got != keep[i_idx, c_idx]))
+        assert bad == 0, f"head {h}: {bad} of {len(got)} keep decisions differ"
+        total += len(got)
+    ref, rl = oracle.attention_dropout(q, ks, onehot, scale, True, W, p, seed, offset, key0=s0)
+    err = float(np.max(np.abs(out.double().cpu().numpy() - ref)))
+    lerr = float(np.max(np.abs(lse.double().cpu().numpy() - rl)))
+    say(f"  {total} decisions agree; out max-abs {err:.3e}, lse max-abs {lerr:.2e}")
+    assert err <= TOL_BF16 / (1.0 - float(np.float32(p))) and lerr <= LSE_TOL

@@ -644,6 +644,20 @@ def test_p14_keep_convention_matches_library_engine(philox_ref):
         assert np.array_equal(keep, want)
 
 
+def test_p14_keep_with_key_offset(philox_ref):
+    # key0 numbers the keys of a slice: the same columns of the full mask, and
+    # the engine addressed per element at key indices near 2^30
+    full = oracle.dropout_keep(3, [0, 7, 40], 150, 0.3, 99, 4)
+    for key0 in (1, 4, 37, 101):
+        part = oracle.dropout_keep(3, [0, 7, 40], 150 - key0, 0.3, 99, 4, key0=key0)
+        assert np.array_equal(part, full[:, key0:])
+    key0, n, rows = (1 << 30) + 3, 21, [5, 2 ** 20]
+    thr = oracle.dropout_threshold(0.4)
+    keep = oracle.dropout_keep(11, rows, n, 0.4, 77, 9, key0=key0)
+    want = philox_ref("keep", [(77, 9, thr, 11, i, key0 + c) for i in rows for c in range(n)])
+    assert np.array_equal(keep, want.reshape(len(rows), n).astype(bool))
+
+
 def test_p14_threshold_and_validation():
     assert oracle.dropout_threshold(0.0) == 0
     assert oracle.dropout_threshold(0.5) == 2 ** 31

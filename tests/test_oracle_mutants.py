@@ -47,6 +47,7 @@ def _pins(ref):
     if ref is not None:
         yield "p14_philox", lambda: T.test_p14_philox_matches_library_engine(ref)
         yield "p14_keep", lambda: T.test_p14_keep_convention_matches_library_engine(ref)
+        yield "p14_keep_key0", lambda: T.test_p14_keep_with_key_offset(ref)
     yield "p14_rate", lambda: [T.test_p14_keep_rate_is_one_minus_p(p) for p in (0.1, 0.9)]
     yield "p14_zero", lambda: [T.test_p14_zero_probability_is_plain_attention(c, w) for c, w in T.MASKS]
     yield "p14_identity", T.test_p14_identity_values_expose_dropped_probabilities
@@ -205,30 +206,32 @@ def _philox_variant(swap_m=False, bump=True, rounds=10, swap_hi_lo=False):
     return philox
 
 
-def _keep_inverted(bh, rows, Lk, p, seed, offset):
-    return ~_orig_keep(bh, rows, Lk, p, seed, offset)
+def _keep_inverted(bh, rows, Lk, p, seed, offset, key0=0):
+    return ~_orig_keep(bh, rows, Lk, p, seed, offset, key0)
 
 
-def _keep_row_key_swapped(bh, rows, Lk, p, seed, offset):
+def _keep_row_key_swapped(bh, rows, Lk, p, seed, offset, key0=0):
     rows = np.asarray(rows)
     thr = OD.dropout_threshold(p)
-    ng = (Lk + 3) // 4
-    ctr = np.zeros((len(rows), ng, 4), dtype=np.uint64)
+    g0, g1 = key0 // 4, (key0 + Lk + 3) // 4
+    ctr = np.zeros((len(rows), g1 - g0, 4), dtype=np.uint64)
     ctr[..., 0] = rows[:, None]
-    ctr[..., 1] = np.arange(ng)[None, :]
+    ctr[..., 1] = np.arange(g0, g1)[None, :]
     ctr[..., 2] = bh
     ctr[..., 3] = offset
-    w = OD.philox4x32(ctr, (seed & 0xFFFFFFFF, seed >> 32)).reshape(len(rows), 4 * ng)[:, :Lk]
-    return w >= thr
+    w = OD.philox4x32(ctr, (seed & 0xFFFFFFFF, seed >> 32)).reshape(len(rows), 4 * (g1 - g0))
+    return w[:, key0 - 4 * g0:key0 - 4 * g0 + Lk] >= thr
 
 
-def _keep_word_order_reversed(bh, rows, Lk, p, seed, offset):
-    full = _orig_keep(bh, rows, 4 * ((Lk + 3) // 4), p, seed, offset)
-    return full.reshape(len(full), -1, 4)[:, :, ::-1].reshape(len(full), -1)[:, :Lk]
+def _keep_word_order_reversed(bh, rows, Lk, p, seed, offset, key0=0):
+    g0 = key0 // 4
+    full = _orig_keep(bh, rows, 4 * ((key0 + Lk + 3) // 4 - g0), p, seed, offset, 4 * g0)
+    rev = full.reshape(len(full), -1, 4)[:, :, ::-1].reshape(len(full), -1)
+    return rev[:, key0 - 4 * g0:key0 - 4 * g0 + Lk]
 
 
 def _attn_drop_variant(mode):
-    def fwd(q, k, v, scale, causal=False, window=-1, p=0.0, seed=0, offset=0, rows=None):
+    def fwd(q, k, v, scale, causal=False, window=-1, p=0.0, seed=0, offset=0, rows=None, key0=0):
         q, k, v = (np.asarray(x, dtype=float) for x in (q, k, v))
         B, Lq, Hq, D = q.shape
         Lk, Hkv = k.shape[1], k.shape[2]
@@ -241,7 +244,7 @@ def _attn_drop_variant(mode):
             for h in range(Hq):
                 g = h // (Hq // Hkv)
                 S = sc * q[b, rr, h] @ k[b, :, g].T
-                keep = OD.dropout_keep(b * Hq + h, rr, Lk, p, seed, offset)
+                keep = OD.dropout_keep(b * Hq + h, rr, Lk, p, seed, offset, key0)
                 P, ls = OA.row_softmax(S, ok & keep if mode == "before_softmax" else ok)
                 Pd = np.where(keep, P, 0.0)
                 if mode == "renormalised":
