@@ -37,6 +37,16 @@
 // step right after its probabilities) and on tile t+1's scores, so the two
 // units overlap inside one wave.
 //
+// Instances of the same kernel:
+//   PAGED  K/V come through a block table from 16-token cache blocks (the
+//          paged prefill); each wave's 16 rows of a tile are one block, and
+//          (sequence, q-block) items of different context lengths are taken
+//          longest first when there are at most 64 of them;
+//   DROP   dropout on the probabilities ("dropout_p" of the flash-attn call
+//          on the «Flash Attention» page): each tile's keep decisions come
+//          from Philox4x32-10 at a per-element counter, drawn at the end of
+//          the previous tile; dropped probabilities still enter the row sum.
+//
 // LDS: 2 stages x (K tile + V tile) x 64 x D x 2 B = 64 KiB at D = 128, so two
 // work-groups fit in the 160 KiB of a CU.  16-byte chunks of each row are
 // XOR-swizzled by row so the MFMA operand reads hit distinct banks.  Each of
