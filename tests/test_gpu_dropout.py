@@ -301,3 +301,40 @@ def test_dropout_backward_workload_std2048(gpu_lib):
         tol = GTOL[cfg.dtype] * max(1.0, float(np.max(np.abs(r)))) / 0.9
         say(f"  {n} max-abs {err:.3e} (tol {tol:.2e})")
         assert err <= tol
+
+
+def _rand_drop_cases(n=12):
+    r = np.random.default_rng(8642)
+    out = []
+    for i in range(n):
+        D = int(r.choice([64, 128]))
+        dtype = str(r.choice(["fp16", "bf16"]))
+        Hkv = int(r.choice([1, 2]))
+        Hq = Hkv * int(r.choice([1, 2, 4]))
+        Lq, Lk = int(r.integers(1, 300)), int(r.integers(1, 300))
+        causal = bool(r.integers(0, 2))
+        window = int(r.choice([-1, -1, 0, 7, 120]))
+        p = float(r.choice([0.05, 0.1, 0.3, 0.5, 0.8]))
+        seed = int(r.integers(0, 2 ** 63))
+        offset = int(r.integers(0, 2 ** 32))
+        out.append((i, int(r.integers(1, 3)), Hq, Hkv, Lq, Lk, D, dtype, causal, window, p, seed, offset))
+    return out
+
+
+@pytest.mark.parametrize("case", _rand_drop_cases(), ids=lambda c: f"r{c[0]}")
+def test_dropout_random_forward_and_backward(gpu_lib, case):
+    i, B, Hq, Hkv, Lq, Lk, D, dtype, causal, window, p, seed, offset = case
+    say(f"[case] dropout random {i}: B{B} Hq{Hq} Hkv{Hkv} Lq{Lq} Lk{Lk} D{D} {dtype} causal{causal} w{window} "
+        f"p{p} seed{seed} off{offset}")
+    q, k, v = random_dense(B, Hq, Hkv, Lq, Lk, D, dtype, 1900 + i)
+    do = _dout(q.shape, dtype, 2000 + i)
+    scale = 1.0 / np.sqrt(D)
+    out, lse = run_drop(gpu_lib, q, k, v, p, seed, offset, scale, causal, window)
+    check_out(f"dropout random {i}", out, lse, q, k, v, scale, causal, window, p, seed, offset, dtype)
+    got = run_bwd_drop(gpu_lib, q, k, v, do, p, seed, offset, scale, causal, window)
+    ref = oracle.attention_dropout_backward(q, k, v, do, scale, causal, window, p, seed, offset)
+    for n, g, r in zip(("dq", "dk", "dv"), got, ref):
+        g = g.double().cpu().numpy()
+        err = float(np.max(np.abs(g - r))) if g.size else 0.0
+        mag = max(1.0, float(np.max(np.abs(r)))) if r.size else 1.0
+        assert err <= GTOL[dtype] * mag / (1.0 - float(np.float32(p))), f"{n}: {err:.3e}"

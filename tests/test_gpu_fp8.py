@@ -116,3 +116,29 @@ def test_fp8_negative_and_zero_scale(gpu_lib, scale):
     say(f"[case] fp8 scale {scale}")
     out, lse = run_fp8(gpu_lib, q, k, v, scale, True, -1, 1.5, 1.0, 0.5)
     check_fp8(f"fp8 scale {scale}", out, lse, q, k, v, scale, True, -1, 1.5, 1.0, 0.5)
+
+
+def _rand_fp8_cases(n=10):
+    r = np.random.default_rng(9753)
+    out = []
+    for i in range(n):
+        D = int(r.choice([64, 128]))
+        Hkv = int(r.choice([1, 2]))
+        Hq = Hkv * int(r.choice([1, 2, 4]))
+        Lq, Lk = int(r.integers(1, 400)), int(r.integers(1, 400))
+        causal = bool(r.integers(0, 2))
+        window = int(r.choice([-1, -1, 0, 9, 150]))
+        qd, kd, vd = (float(x) for x in r.choice([0.25, 0.5, 1.0, 2.0], size=3))
+        out.append((i, int(r.integers(1, 3)), Hq, Hkv, Lq, Lk, D, causal, window, qd, kd, vd))
+    return out
+
+
+@pytest.mark.parametrize("case", _rand_fp8_cases(), ids=lambda c: f"r{c[0]}")
+def test_fp8_random(gpu_lib, case):
+    i, B, Hq, Hkv, Lq, Lk, D, causal, window, qd, kd, vd = case
+    say(f"[case] fp8 random {i}: B{B} Hq{Hq} Hkv{Hkv} Lq{Lq} Lk{Lk} D{D} causal{causal} w{window} "
+        f"descale {qd},{kd},{vd}")
+    cfg = DenseConfig(f"fp8_r{i}", B, Hq, Hkv, Lq, Lk, D, "fp8", causal, window, 980 + i)
+    q, k, v = dense_inputs(cfg)
+    out, lse = run_fp8(gpu_lib, q, k, v, cfg.scale, causal, window, qd, kd, vd)
+    check_fp8(f"fp8 random {i}", out, lse, q, k, v, cfg.scale, causal, window, qd, kd, vd)
