@@ -97,16 +97,22 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecArgs a) {
   const int cap = a.max_blocks_per_seq * C::BS;
 
   // ---- 1. block counts of all sequences -> inclusive prefix in LDS.
-  // Thread t takes the run of up to 8 sequences [8t, 8t+8).
+  // Thread t takes the run of up to 8 sequences [8t, 8t+8).  Every load is
+  // unconditional at an index clamped into [0, ns) (ns >= 1), so all eight
+  // are in flight together instead of one guarded load after another;
+  // entries past the launch's last sequence then count as empty.
   int nbv[8];
   int local = 0;
   const int s_beg = tid * 8;
+  {
+    int cl[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int s = s_beg + i;
-    const int c = s < ns ? min(max(a.ctx_lens[s], 0), cap) : 0;
-    nbv[i] = (c + C::BS - 1) / C::BS;
-    local += nbv[i];
+    for (int i = 0; i < 8; ++i) cl[i] = a.ctx_lens[min(s_beg + i, ns - 1)];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      nbv[i] = s_beg + i < ns ? (min(max(cl[i], 0), cap) + C::BS - 1) / C::BS : 0;
+      local += nbv[i];
+    }
   }
   int x = local;
 #pragma unroll
@@ -181,15 +187,19 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecArgs a) {
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) oacc[db] = f32x4{};
   float m_ref = -INFINITY, l_run = 0.f;
+  // Query operand of the sequence being computed (qcur), and one landing
+  // buffer per pipeline slot: a unit that starts a sequence (or a window)
+  // loads that sequence's query rows into its slot's buffer together with
+  // its K/V tiles, so the load overlaps the units ahead of it, and its
+  // compute step takes them over.  These are compiler-visible loads, so the
+  // compiler places the wait before their first use.
   u32x4_t qcur[C::KS];
+  u32x4_t qs[C::DEPTH][C::KS];
   // Query operand for sequence s: 16-byte chunks KS*G + ks of head hj.
-  auto load_q_sync = [&](int s) {
+  auto load_q = [&](int s, u32x4_t(&dst)[C::KS]) {
     const rsrc_t rq = make_rsrc((const E*)a.q + ((size_t)s * a.Hq + g * a.group) * D, (uint32_t)(a.group * C::ROW));
-    uint32_t qo[C::KS];
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) qo[ks] = qoff + 16 * ks;
-    if constexpr (C::KS == 4) buf_load16_x4_sync(qcur, rq, qo);
-    else buf_load16_x2_sync(qcur, rq, qo);
+    for (int ks = 0; ks < C::KS; ++ks) dst[ks] = __builtin_bit_cast(u32x4_t, buf_load16(rq, qoff + 16 * ks));
   };
 
   // Windows of up to 64 units: lane i describes unit i.  The loads of the
@@ -221,12 +231,11 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecArgs a) {
       const int whole = (r_beg <= excl) && (r_end >= incl);
       u_fl = first | (last << 1) | (whole << 2);
     }
-    // The window's first sequence: its query rows, before any tile load.
-    load_q_sync(__builtin_amdgcn_readlane(u_s, 0));
-
-    // K and V tiles of unit u into pipeline slot J.
+    // K and V tiles of unit u into pipeline slot J, preceded by the query
+    // rows when the unit starts a sequence or the window.
     auto issue = [&](int u, auto slot) {
       constexpr int J = decltype(slot)::value;
+      if (u == 0 || (__builtin_amdgcn_readlane(u_fl, u) & 1)) load_q(__builtin_amdgcn_readlane(u_s, u), qs[J]);
       E* kd = (J == 0 ? kb0 : J == 1 ? kb1 : J == 2 ? kb2 : kb3) + wave * C::TILE;
       E* vd = (J == 0 ? vb0 : J == 1 ? vb1 : J == 2 ? vb2 : vb3) + wave * C::TILE;
       const int pb = __builtin_amdgcn_readlane(u_pb, u);
@@ -247,9 +256,10 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecArgs a) {
       const int ntok = __builtin_amdgcn_readlane(u_ntok, u);
       const int fl = __builtin_amdgcn_readlane(u_fl, u);
       const int s = __builtin_amdgcn_readlane(u_s, u);
-      // A sequence starting inside the window: reload the query rows (this
-      // waits for every load in flight; it happens once per sequence start).
-      if ((fl & 1) && u > 0) load_q_sync(s);
+      if (u == 0 || (fl & 1)) {
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) qcur[ks] = qs[J][ks];
+      }
       const int after = min(n - 1 - u, C::DEPTH - 1);  // units issued after this one
       if (after >= 3) wait_vm<3 * C::OPS>();
       else if (after == 2) wait_vm<2 * C::OPS>();
@@ -383,12 +393,12 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int j = j0 + 64 * i + lane;
-      c[i] = j < a.num_seqs ? a.ctx_lens[j] : 0;
+      c[i] = a.ctx_lens[min(j, a.num_seqs - 1)];  // unconditional, so the 8 loads overlap
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int j = j0 + 64 * i + lane;
-      const int nb = (min(max(c[i], 0), cap) + 15) >> 4;
+      const int nb = j < a.num_seqs ? (min(max(c[i], 0), cap) + 15) >> 4 : 0;
       tot += nb;
       bef += j < s ? nb : 0;
     }
