@@ -100,7 +100,8 @@ int fwd_dense(const void* q, const void* k, const void* v, void* out, float* lse
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return ATTN_ERR_ALIGN;
   if (lse && !aligned(lse, 4)) return ATTN_ERR_ALIGN;
   if (q_empty) return ATTN_OK;  // nothing to compute
-  const int dev = check_device();
+  int cus = 0;
+  const int dev = check_device(&cus);
   if (dev != ATTN_OK) return dev;
 
   attn::FwdArgs a;
@@ -121,6 +122,9 @@ int fwd_dense(const void* q, const void* k, const void* v, void* out, float* lse
   a.seed_lo = (uint32_t)seed;
   a.seed_hi = (uint32_t)(seed >> 32);
   a.drop_offset = offset;
+  // A grid of at most one work-group per CU leaves each SIMD one wave; the
+  // key-split instance then gives every work-group 8 waves.
+  a.kv_split = n_qblocks * Hq * (long long)B <= cus ? 1 : 0;
   hipError_t e = drop ? attn::launch_fwd_dropout(a, D, dtype, (hipStream_t)stream)
                       : attn::launch_fwd(a, D, dtype, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
@@ -200,7 +204,8 @@ ATTN_API int attn_fwd_paged(const void* q, const void* k_cache, const void* v_ca
   if (!aligned(block_table, 4) || !aligned(ctx_lens, 4)) return ATTN_ERR_ALIGN;
   if (lse && !aligned(lse, 4)) return ATTN_ERR_ALIGN;
   if (empty) return ATTN_OK;
-  const int dev = check_device();
+  int cus = 0;
+  const int dev = check_device(&cus);
   if (dev != ATTN_OK) return dev;
 
   attn::FwdArgs a;
@@ -215,6 +220,9 @@ ATTN_API int attn_fwd_paged(const void* q, const void* k_cache, const void* v_ca
   a.ctx_lens = ctx_lens;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_blocks = num_blocks;
+  a.drop_thr = a.seed_lo = a.seed_hi = a.drop_offset = 0u;
+  a.drop_scale = 1.f;
+  a.kv_split = n_qblocks * Hq * (long long)B <= cus ? 1 : 0;
   hipError_t e = attn::launch_fwd_paged(a, D, dtype, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }

@@ -98,20 +98,30 @@ __device__ __forceinline__ int v_swz(int r) {
 constexpr float kRescaleThreshold = 8.0f;
 
 
-template <typename TT, int D, bool PAGED, bool DROP>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
+template <typename TT, int D, bool PAGED, bool DROP, bool SPLIT>
+__global__ __launch_bounds__(SPLIT ? 512 : 256, SPLIT ? 1 : 2) void fwd_kernel(FwdArgs a) {
   using C = FwdCfg<D>;
   using E = typename TT::elem;
   using V8 = typename TT::vec8;
   using V4 = typename TT::vec4;
-  __shared__ __attribute__((aligned(16))) E kt0[C::TILE];
-  __shared__ __attribute__((aligned(16))) E kt1[C::TILE];
-  __shared__ __attribute__((aligned(16))) E vt0[C::TILE];
-  __shared__ __attribute__((aligned(16))) E vt1[C::TILE];
+  // SPLIT: 8 waves; waves 4h..4h+3 (half h) take the key tiles t_lo + h,
+  // t_lo + h + 2, ... of the same 128 query rows, each half with its own
+  // tile buffers, and half 1 hands its (max, sum, output) to half 0 through
+  // LDS at the end.  Used when the grid is too small to give every SIMD two
+  // waves; otherwise SPLIT is false and each work-group walks all tiles.
+  constexpr int NH = SPLIT ? 2 : 1;  // key halves
+  constexpr int TS = NH;             // tile stride of one half
+  __shared__ __attribute__((aligned(16))) E kt0[NH * C::TILE];
+  __shared__ __attribute__((aligned(16))) E kt1[NH * C::TILE];
+  __shared__ __attribute__((aligned(16))) E vt0[NH * C::TILE];
+  __shared__ __attribute__((aligned(16))) E vt1[NH * C::TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keep it scalar
+  const int wave_id = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keep it scalar
+  const int wave = wave_id & 3;                  // 32-row group of the work-group's 128 rows
+  const int hf = SPLIT ? (wave_id >> 2) : 0;     // key half
+  const int hoff = hf * C::TILE;                 // this half's tile buffers
   const int hh = lane >> 5, l32 = lane & 31;
   const int j16 = lane & 15, grp = lane >> 4;
 
@@ -232,14 +242,14 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   // ---- per-lane LDS element offsets inside a tile
   int koff[C::KSTEPS];  // K operand of k-step s, first 32-key half (+32*D for the second)
 #pragma unroll
-  for (int s = 0; s < C::KSTEPS; ++s) koff[s] = l32 * D + (((2 * s + hh) ^ k_swz<D>(l32)) << 3);
+  for (int s = 0; s < C::KSTEPS; ++s) koff[s] = hoff + l32 * D + (((2 * s + hh) ^ k_swz<D>(l32)) << 3);
   int voff[C::DB];      // V transposed read for d-block d, rows 4*hh + j16/4 (+16*s, +8)
   {
     const int r = 4 * hh + (j16 >> 2);
 #pragma unroll
     for (int d = 0; d < C::DB; ++d) {
       const int col = 32 * d + 16 * (grp & 1) + 4 * (j16 & 3);
-      voff[d] = r * D + ((((col >> 3) ^ v_swz<D>(r)) << 3) + 4 * ((col >> 2) & 1));
+      voff[d] = hoff + r * D + ((((col >> 3) ^ v_swz<D>(r)) << 3) + 4 * ((col >> 2) & 1));
     }
   }
 
@@ -301,17 +311,18 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     if constexpr (PAGED) r = block_rsrc(kb, t, entry);
     else r = make_rsrc(kb + (size_t)t * C::BN * kv_rs, tile_bytes(t));
 #pragma unroll
-    for (int i = 0; i < IPW; ++i) buf_load16_lds(r, ksrc[i], dst + (wave * IPW + i) * RPI * D);
+    for (int i = 0; i < IPW; ++i) buf_load16_lds(r, ksrc[i], dst + hoff + (wave * IPW + i) * RPI * D);
   };
   auto load_v = [&](int t, E* dst, int entry) {
     rsrc_t r;
     if constexpr (PAGED) r = block_rsrc(vb, t, entry);
     else r = make_rsrc(vb + (size_t)t * C::BN * kv_rs, tile_bytes(t));
 #pragma unroll
-    for (int i = 0; i < IPW; ++i) buf_load16_lds(r, vsrc[i], dst + (wave * IPW + i) * RPI * D);
+    for (int i = 0; i < IPW; ++i) buf_load16_lds(r, vsrc[i], dst + hoff + (wave * IPW + i) * RPI * D);
   };
   // Paged: table entries for the next K and V tile loads (K(t+2) and V(t+1)
-  // at tile t); each tile fetches the entry of K(t+3), one tile ahead of use.
+  // at tile t); each tile fetches the entry of K(t+3), one tile ahead of use
+  // (with SPLIT, the tiles of this half: t+4, t+2 and t+6).
   int eK = 0, eV = 0;
 
   // Does every row of this wave see every key of tile t?  (Wave-uniform.)
@@ -377,7 +388,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   f32x16 scur[2];           // raw scores of the current tile, masked
   float mx_cur = -INFINITY; // their row maximum
 
-  // One tile: K(t+2) and V(t+1) start loading into the buffers K(t) and
+  // One tile (with SPLIT, "t+1" and "t+2" below are this half's next tiles,
+  // t+2 and t+4): K(t+2) and V(t+1) start loading into the buffers K(t) and
   // V(t-1) left; tile t's statistics update; then, per 16-key step s, the
   // step's probabilities (exp2 of one FMA on the raw scores), its P.V MFMAs,
   // and a quarter of tile t+1's S^T = K Q^T.  The key order inside a step is
@@ -401,10 +413,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     read_k(0);
     read_k(1);
     __builtin_amdgcn_sched_barrier(0);
-    load_k(t + 2, P ? kt1 : kt0, eK);
-    load_v(t + 1, P ? vt0 : vt1, eV);
+    load_k(t + 2 * TS, P ? kt1 : kt0, eK);
+    load_v(t + TS, P ? vt0 : vt1, eV);
     int eN = 0;
-    if constexpr (PAGED) eN = fetch_entry(t + 3);
+    if constexpr (PAGED) eN = fetch_entry(t + 3 * TS);
 
     // Move the exponent base only when the maximum has grown by more than
     // the threshold somewhere in the wave; rescale those rows.
@@ -526,16 +538,16 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     const float mnext = max_xor32(fmaxf(mx_a, mx_b));
     l_run += rs;
     mx_cur = mnext;
-    if (!tile_full(t + 1)) {
+    if (!tile_full(t + TS)) {
       asm volatile("" ::: "memory");  // a real branch: the mask is rare, do not speculate it
-      mask_tile(t + 1, snext);
+      mask_tile(t + TS, snext);
       mx_cur = row_max(snext);
     }
     scur[0] = snext[0];
     scur[1] = snext[1];
     // The next tile's dropout decisions, while its loads complete (few
     // registers are live here).
-    if constexpr (DROP) kbits = draw_tile(t + 1);
+    if constexpr (DROP) kbits = draw_tile(t + TS);
     wait_vmem();
     __syncthreads();
     __builtin_amdgcn_s_setprio(0);
@@ -547,16 +559,16 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 
   if (t_lo < t_hi) {
     if constexpr (PAGED) {
-      const int e0 = fetch_entry(t_lo), e1 = fetch_entry(t_lo + 1);
-      eK = fetch_entry(t_lo + 2);
+      const int e0 = fetch_entry(t_lo + hf), e1 = fetch_entry(t_lo + hf + TS);
+      eK = fetch_entry(t_lo + hf + 2 * TS);
       eV = e1;
-      load_k(t_lo, kt0, e0);
-      load_v(t_lo, vt0, e0);
-      load_k(t_lo + 1, kt1, e1);
+      load_k(t_lo + hf, kt0, e0);
+      load_v(t_lo + hf, vt0, e0);
+      load_k(t_lo + hf + TS, kt1, e1);
     } else {
-      load_k(t_lo, kt0, 0);
-      load_v(t_lo, vt0, 0);
-      load_k(t_lo + 1, kt1, 0);
+      load_k(t_lo + hf, kt0, 0);
+      load_v(t_lo + hf, vt0, 0);
+      load_k(t_lo + hf + TS, kt1, 0);
     }
     wait_vmem();
     __syncthreads();
@@ -570,14 +582,51 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         scur[kh] = TT::mfma32(kf, qf[s], scur[kh]);
       }
     }
-    if (!tile_full(t_lo)) mask_tile(t_lo, scur);
+    // (SPLIT: half 1's first tile may lie past the range when the range
+    // holds one tile; it then loaded zeros and is masked whole.)
+    if (!tile_full(t_lo + hf)) mask_tile(t_lo + hf, scur);
     mx_cur = row_max(scur);
-    if constexpr (DROP) kbits = draw_tile(t_lo);
+    if constexpr (DROP) kbits = draw_tile(t_lo + hf);
     __syncthreads();  // K(t_lo)'s buffer is refilled by the first tile
   }
-  for (int t = t_lo; t < t_hi; t += 2) {
-    body(t, Par<0>{});
-    if (t + 1 < t_hi) body(t + 1, Par<1>{});
+  // Both halves run the same number of bodies (the barriers inside are the
+  // work-group's): with an odd tile count half 1's last one lies past the
+  // range, loads zeros and is masked whole, so it adds nothing.
+  const int n_it = (t_hi - t_lo + NH - 1) / NH;
+  for (int i = 0; i < n_it; i += 2) {
+    body(t_lo + hf + i * TS, Par<0>{});
+    if (i + 1 < n_it) body(t_lo + hf + (i + 1) * TS, Par<1>{});
+  }
+
+  if constexpr (SPLIT) {
+    // Every load has landed and every wave has passed the last barrier, so
+    // the tile buffers are free.  Half 1 leaves, per lane, its output block
+    // d in buffer d (kt0, kt1, vt0, vt1 in turn) and its exponent base and
+    // sum after that; half 0's wave of the same rows reads them lane for
+    // lane and merges: m = max(m0, m1), each side scaled by 2^(m_side - m).
+    float* xo[4] = {(float*)kt0, (float*)kt1, (float*)vt0, (float*)vt1};
+    float* xs = (float*)(C::DB == 4 ? vt1 : vt0) + (C::DB == 4 ? 16 : 0) * 256;
+    const int xi = wave * 64 + lane;  // 256 lanes of a half
+    if (hf == 1) {
+#pragma unroll
+      for (int d = 0; d < C::DB; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xo[d][r * 256 + xi] = oacc[d][r];
+      xs[xi] = m_ref;
+      xs[256 + xi] = l_run;
+    }
+    __syncthreads();
+    if (hf == 1) return;
+    const float m1 = xs[xi], l1 = xs[256 + xi];
+    const float mm = fmaxf(m_ref, m1);
+    const float a0 = m_ref == -INFINITY ? 0.f : fast_exp2(m_ref - mm);
+    const float a1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - mm);
+    l_run = a0 * l_run + a1 * l1;
+#pragma unroll
+    for (int d = 0; d < C::DB; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[d][r] = a0 * oacc[d][r] + a1 * xo[d][r * 256 + xi];
+    m_ref = mm;
   }
 
   // ---- epilogue: normalise, store O in the input type, and the log-sum-exp
@@ -600,29 +649,39 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   }
 }
 
-template <typename TT, int D, bool PAGED, bool DROP = false>
+template <typename TT, int D, bool PAGED, bool DROP = false, bool SPLIT = false>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   const long long blocks = (long long)a.n_qblocks * a.Hq * a.B;
-  hipLaunchKernelGGL((fwd_kernel<TT, D, PAGED, DROP>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((fwd_kernel<TT, D, PAGED, DROP, SPLIT>), dim3((unsigned)blocks), dim3(SPLIT ? 512 : 256), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
-hipError_t launch_fwd(const FwdArgs& a, int D, int dtype, hipStream_t stream) {
+// The key-split instance serves grids of at most one work-group per CU
+// (kv_split), for every entry point of this kernel, so that the dense,
+// paged and dropout forwards of one shape stay the same arithmetic.
+template <typename TT, int D, bool PAGED, bool DROP>
+static hipError_t launch_fwd_s(const FwdArgs& a, hipStream_t stream) {
+  return a.kv_split ? launch_fwd_t<TT, D, PAGED, DROP, true>(a, stream) : launch_fwd_t<TT, D, PAGED, DROP>(a, stream);
+}
+
+template <bool PAGED, bool DROP>
+static hipError_t launch_fwd_any(const FwdArgs& a, int D, int dtype, hipStream_t stream) {
   if (dtype == 1)
-    return D == 128 ? launch_fwd_t<BF16, 128, false>(a, stream) : launch_fwd_t<BF16, 64, false>(a, stream);
-  return D == 128 ? launch_fwd_t<F16, 128, false>(a, stream) : launch_fwd_t<F16, 64, false>(a, stream);
+    return D == 128 ? launch_fwd_s<BF16, 128, PAGED, DROP>(a, stream) : launch_fwd_s<BF16, 64, PAGED, DROP>(a, stream);
+  return D == 128 ? launch_fwd_s<F16, 128, PAGED, DROP>(a, stream) : launch_fwd_s<F16, 64, PAGED, DROP>(a, stream);
+}
+
+hipError_t launch_fwd(const FwdArgs& a, int D, int dtype, hipStream_t stream) {
+  return launch_fwd_any<false, false>(a, D, dtype, stream);
 }
 
 hipError_t launch_fwd_dropout(const FwdArgs& a, int D, int dtype, hipStream_t stream) {
-  if (dtype == 1)
-    return D == 128 ? launch_fwd_t<BF16, 128, false, true>(a, stream) : launch_fwd_t<BF16, 64, false, true>(a, stream);
-  return D == 128 ? launch_fwd_t<F16, 128, false, true>(a, stream) : launch_fwd_t<F16, 64, false, true>(a, stream);
+  return launch_fwd_any<false, true>(a, D, dtype, stream);
 }
 
 hipError_t launch_fwd_paged(const FwdArgs& a, int D, int dtype, hipStream_t stream) {
-  if (dtype == 1)
-    return D == 128 ? launch_fwd_t<BF16, 128, true>(a, stream) : launch_fwd_t<BF16, 64, true>(a, stream);
-  return D == 128 ? launch_fwd_t<F16, 128, true>(a, stream) : launch_fwd_t<F16, 64, true>(a, stream);
+  return launch_fwd_any<true, false>(a, D, dtype, stream);
 }
 
 }  // namespace attn

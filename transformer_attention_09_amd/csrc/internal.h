@@ -31,6 +31,9 @@ struct FwdArgs {
   // are scaled by drop_scale = 1/(1-p).  Unused by the other entry points.
   uint32_t drop_thr, seed_lo, seed_hi, drop_offset;
   float drop_scale;
+  // Split each work-group's key tiles between two 4-wave halves (set when
+  // the grid has no more work-groups than the device has CUs).
+  int kv_split;
 };
 
 // Paged decode.  The cache blocks of all sequences, taken in sequence order,
