@@ -205,6 +205,28 @@ def test_deterministic_bitwise(gpu_lib):
     assert torch.equal(a, b) and torch.equal(la, lb)
 
 
+@pytest.mark.parametrize("Lk,causal,window", [(150, False, -1), (200, True, -1), (321, False, 70), (64, True, 0)])
+def test_key_split_boundary(gpu_lib, Lk, causal, window):
+    """A grid of exactly one work-group per CU runs the key-split instance
+    (two 4-wave halves over alternate key tiles); one more work-group runs
+    the plain one.  The same heads go through both: each result matches the
+    oracle, and the shared heads agree with each other to the tolerance.
+    Odd tile counts (150 keys: 3 tiles) leave half 1 a tile past the range."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    Lq, D, dtype = 128, 64, "fp16"
+    say(f"[case] key split boundary: {cus} vs {cus + 1} work-groups, Lk {Lk} causal {causal} window {window}")
+    q, k, v = random_dense(1, cus + 1, 1, Lq, Lk, D, dtype, seed=77)
+    scale = 1.0 / math.sqrt(D)
+    split_o, split_l = run_fwd(gpu_lib, q[:, :, :cus].contiguous(), k, v, scale, causal, window)
+    full_o, full_l = run_fwd(gpu_lib, q, k, v, scale, causal, window)
+    heads = np.unique(np.r_[0, 1, cus // 2, cus - 1, np.random.default_rng(Lk).integers(0, cus, 12)])
+    ro, rl = oracle.attention(q[:, :, heads].contiguous(), k, v, scale, causal, window)
+    check("split instance", split_o[:, :, heads], split_l[:, heads], ro, rl, dtype)
+    check("plain instance", full_o[:, :, heads], full_l[:, heads], ro, rl, dtype)
+    d = (split_o.double() - full_o[:, :, :cus].double()).abs().max().item()
+    assert d <= TOL[dtype], f"split and plain instances differ by {d:.3e}"
+
+
 def test_constant_v_gives_v(gpu_lib):
     q, k, _ = random_dense(1, 4, 4, 190, 190, 64, "bf16", seed=9)
     v = torch.full((1, 190, 4, 64), 0.8125, dtype=torch.bfloat16)
