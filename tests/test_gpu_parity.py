@@ -150,6 +150,21 @@ def test_random_small(gpu_lib, case):
     check(f"random{i}", out, lse, ro, rl, dtype)
 
 
+@pytest.mark.parametrize("B,H,Lq,Lk,D,dtype,window", [(8, 3, 200, 300, 128, "bf16", 100), (16, 24, 130, 77, 64, "fp16", -1),
+                                                      (24, 2, 257, 257, 64, "bf16", -1)])
+def test_batch_rows_per_xcd(gpu_lib, B, H, Lq, Lk, D, dtype, window):
+    """Multi-head (no GQA), non-causal, batch a multiple of 8: the work-groups
+    of each batch row go to one XCD.  Small grids (key-split instance) and
+    large ones, against the oracle on a few batch rows."""
+    say(f"[case] batch rows per XCD: B{B} H{H} Lq{Lq} Lk{Lk} D{D} {dtype} window {window}")
+    q, k, v = random_dense(B, H, H, Lq, Lk, D, dtype, seed=B + H)
+    scale = 1.0 / math.sqrt(D)
+    out, lse = run_fwd(gpu_lib, q, k, v, scale, False, window)
+    rows = [0, 5, B - 1]
+    ro, rl = oracle.attention(q[rows], k[rows], v[rows], scale, False, window)
+    check("batch rows per XCD", out[rows], lse[rows], ro, rl, dtype)
+
+
 # ------------------------------------------------------------ edge cases
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])

@@ -22,7 +22,9 @@
 //   keys) pay for an element-wise mask.  Work-group ids go round-robin over
 //   the 8 XCDs; when the KV groups divide evenly, each XCD takes whole KV
 //   groups (the query heads sharing one K/V stay in one L2) and issues its
-//   q-blocks heaviest first (causal).
+//   q-blocks heaviest first (causal).  Without GQA and without the causal
+//   mask, whole batch rows go to one XCD instead (all heads of a token range
+//   are read there together).
 //
 // Per 64-key tile and wave (all MFMA 32x32x16, fp32 accumulate):
 //   S^T = K Q^T  : A = K rows from LDS, B = the wave's Q rows (registers).
@@ -129,7 +131,18 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256, SPLIT ? 1 : 2) void fwd_kernel(F
   int qb_rank, gid, hj;
   {
     const int n_groups = a.B * a.Hkv;
-    if ((n_groups & 7) == 0) {
+    if (!PAGED && !a.causal && a.group == 1 && (a.B & 7) == 0) {
+      // No K/V is shared between heads, and no q-block outweighs another:
+      // XCD x takes the batch rows x, x+8, ... and walks (batch, q-block,
+      // head), so the heads of one token range, which sit side by side in
+      // memory, are read by one XCD at about the same time.
+      const int x = blockIdx.x & 7, k = blockIdx.x >> 3;
+      const int per_b = a.n_qblocks * a.Hq;
+      const int bl = k / per_b, r = k - bl * per_b;
+      qb_rank = r / a.Hq;
+      gid = (x + 8 * bl) * a.Hkv + (r - qb_rank * a.Hq);
+      hj = 0;
+    } else if ((n_groups & 7) == 0) {
       // XCD x (= blockIdx mod 8) takes the KV groups x, x+8, ...; its
       // work-groups walk q-block ranks, heaviest first when causal.
       const int x = blockIdx.x & 7, k = blockIdx.x >> 3;
