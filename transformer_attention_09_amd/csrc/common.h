@@ -226,6 +226,41 @@ __device__ __forceinline__ uint32_t pack2<F16>(float a, float b) {
   return __builtin_bit_cast(uint32_t, (v2){(_Float16)a, (_Float16)b});
 }
 
+// One output row of the 32x32 MFMA accumulator layout, scaled by inv and
+// rounded to the element type.  Lane l (row l mod 32, half hh = l / 32) holds
+// columns 32*d + 8*q + 4*hh + 0..3 in registers 4q..4q+3 of block d, so lanes
+// l and l^32 each hold half of every 8 columns.  One v_permlane32_swap per
+// packed dword gives the low half-wave the 8 columns of q = 0 and 2 and the
+// high half-wave those of q = 1 and 3, and each lane stores 16-byte pieces.
+// The swaps run in every lane; store selects the lanes that write.
+template <typename TT, int DB>
+__device__ __forceinline__ void store_row16(void* orow, const f32x16 (&acc)[DB], float inv, int hh, bool store) {
+  uint4 w[DB][2];
+#pragma unroll
+  for (int d = 0; d < DB; ++d) {
+#pragma unroll
+    for (int qp = 0; qp < 2; ++qp) {
+      uint32_t e[2][2];  // [q = 2*qp + i][dword]
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int q = 2 * qp + i;
+        e[i][0] = pack2<TT>(acc[d][4 * q] * inv, acc[d][4 * q + 1] * inv);
+        e[i][1] = pack2<TT>(acc[d][4 * q + 2] * inv, acc[d][4 * q + 3] * inv);
+      }
+      const auto x = __builtin_amdgcn_permlane32_swap(e[0][0], e[1][0], false, false);
+      const auto y = __builtin_amdgcn_permlane32_swap(e[0][1], e[1][1], false, false);
+      w[d][qp] = make_uint4(x[0], y[0], x[1], y[1]);
+    }
+  }
+  if (store) {
+    uint16_t* o = (uint16_t*)orow;  // 16-bit elements
+#pragma unroll
+    for (int d = 0; d < DB; ++d)
+#pragma unroll
+      for (int qp = 0; qp < 2; ++qp) *(uint4*)(o + 32 * d + 16 * qp + 8 * hh) = w[d][qp];
+  }
+}
+
 template <typename V4, typename V8>
 __device__ __forceinline__ V8 cat4(V4 lo, V4 hi) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);

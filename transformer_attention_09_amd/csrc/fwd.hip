@@ -646,34 +646,8 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256, SPLIT ? 1 : 2) void fwd_kernel(F
   const float lt = sum_xor32(l_run);
   float inv = lt > 0.f ? 1.f / lt : 0.f;
   if constexpr (DROP) inv *= a.drop_scale;
-  // Lane l holds columns 32d + 8q + 4*hh + 0..3 of its row and lane l^32 the
-  // other four of each 8.  One v_permlane32_swap per packed dword hands the
-  // low half-wave the 8 columns of q = 0 (2) and the high half-wave those of
-  // q = 1 (3), so every lane stores whole 16-byte pieces.
-  uint4 ow[C::DB][2];
-#pragma unroll
-  for (int d = 0; d < C::DB; ++d) {
-#pragma unroll
-    for (int qp = 0; qp < 2; ++qp) {
-      uint32_t e[2][2];  // [q4 = 2qp + i][dword]
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int q4 = 2 * qp + i;
-        e[i][0] = pack2<TT>(oacc[d][4 * q4] * inv, oacc[d][4 * q4 + 1] * inv);
-        e[i][1] = pack2<TT>(oacc[d][4 * q4 + 2] * inv, oacc[d][4 * q4 + 3] * inv);
-      }
-      const auto x = __builtin_amdgcn_permlane32_swap(e[0][0], e[1][0], false, false);
-      const auto y = __builtin_amdgcn_permlane32_swap(e[0][1], e[1][1], false, false);
-      ow[d][qp] = make_uint4(x[0], y[0], x[1], y[1]);
-    }
-  }
+  store_row16<TT, C::DB>((E*)a.o + ((size_t)((size_t)b * a.Lq + qi) * a.Hq + hq) * D, oacc, inv, hh, qi < a.Lq);
   if (qi < a.Lq) {
-    E* orow = (E*)a.o + ((size_t)((size_t)b * a.Lq + qi) * a.Hq + hq) * D;
-#pragma unroll
-    for (int d = 0; d < C::DB; ++d) {
-#pragma unroll
-      for (int qp = 0; qp < 2; ++qp) *(uint4*)(orow + 32 * d + 16 * qp + 8 * hh) = ow[d][qp];
-    }
     if (a.lse != nullptr && hh == 0)
       a.lse[((size_t)b * a.Hq + hq) * a.Lq + qi] = lt > 0.f ? (m_ref + log2f(lt)) * kLn2 : -INFINITY;
   }

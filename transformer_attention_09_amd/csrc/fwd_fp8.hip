@@ -276,17 +276,8 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(F8Args a) {
   // Epilogue: O = dv * O^T / l in bf16; lse in natural log units.
   const float lt = sum_xor32(l_run);
   const float inv = lt > 0.f ? a.v_descale / lt : 0.f;
+  store_row16<BF16, C::DT>((__bf16*)a.o + (((size_t)b * a.Lq + qi) * a.Hq + hq) * D, oacc, inv, hh, qi < a.Lq);
   if (qi < a.Lq) {
-    __bf16* orow = (__bf16*)a.o + (((size_t)b * a.Lq + qi) * a.Hq + hq) * D;
-#pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) {
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const uint2 w = make_uint2(pack2<BF16>(oacc[dt][4 * q4] * inv, oacc[dt][4 * q4 + 1] * inv),
-                                   pack2<BF16>(oacc[dt][4 * q4 + 2] * inv, oacc[dt][4 * q4 + 3] * inv));
-        *(uint2*)(orow + 32 * dt + 8 * q4 + 4 * hh) = w;
-      }
-    }
     if (a.lse != nullptr && hh == 0)
       a.lse[((size_t)b * a.Hq + hq) * a.Lq + qi] = lt > 0.f ? (m_ref + log2f(lt)) * kLn2 : -INFINITY;
   }
