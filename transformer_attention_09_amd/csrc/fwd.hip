@@ -47,7 +47,10 @@
 //   DROP   dropout on the probabilities ("dropout_p" of the flash-attn call
 //          on the «Flash Attention» page): each tile's keep decisions come
 //          from Philox4x32-10 at a per-element counter, drawn at the end of
-//          the previous tile; dropped probabilities still enter the row sum.
+//          the previous tile; dropped probabilities still enter the row sum;
+//   SPLIT  for grids of at most one work-group per CU (any of the above):
+//          8 waves, two 4-wave halves over alternate key tiles of the same
+//          rows, merged through LDS at the end (two waves per SIMD).
 //
 // LDS: 2 stages x (K tile + V tile) x 64 x D x 2 B = 64 KiB at D = 128, so two
 // work-groups fit in the 160 KiB of a CU.  16-byte chunks of each row are
