@@ -370,11 +370,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
         }
     }
     __syncthreads();
-    if (rh == 0 && kw0 + l32 < a.Lk) {
-      const size_t ro = (((size_t)b * a.Lk + kw0 + l32) * a.Hkv + g) * D;
-      E* dkr = (E*)a.dk + ro;
-      E* dvr = (E*)a.dv + ro;
-      const float sc = a.scale;
+    if (rh == 0) {
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) {
 #pragma unroll
@@ -382,14 +378,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
           const int j = dt * 4 + q4;
           const f32x4 ok = *(const f32x4*)(pk + (j * 64 + lane) * 4);
           const f32x4 ov = *(const f32x4*)(pv + (j * 64 + lane) * 4);
-          *(uint2*)(dkr + 32 * dt + 8 * q4 + 4 * hh) =
-              make_uint2(pack2<TT>((dkacc[dt][4 * q4] + ok[0]) * sc, (dkacc[dt][4 * q4 + 1] + ok[1]) * sc),
-                         pack2<TT>((dkacc[dt][4 * q4 + 2] + ok[2]) * sc, (dkacc[dt][4 * q4 + 3] + ok[3]) * sc));
-          *(uint2*)(dvr + 32 * dt + 8 * q4 + 4 * hh) =
-              make_uint2(pack2<TT>(dvacc[dt][4 * q4] + ov[0], dvacc[dt][4 * q4 + 1] + ov[1]),
-                         pack2<TT>(dvacc[dt][4 * q4 + 2] + ov[2], dvacc[dt][4 * q4 + 3] + ov[3]));
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            dkacc[dt][4 * q4 + r] += ok[r];
+            dvacc[dt][4 * q4 + r] += ov[r];
+          }
         }
       }
+      const size_t ro = (((size_t)b * a.Lk + kw0 + l32) * a.Hkv + g) * D;
+      const bool key_ok = kw0 + l32 < a.Lk;
+      store_row16<TT, C::DT>((E*)a.dk + ro, dkacc, a.scale, hh, key_ok);
+      store_row16<TT, C::DT>((E*)a.dv + ro, dvacc, 1.f, hh, key_ok);
     }
   }
 }
@@ -584,19 +583,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     }
   }
 
-  if (qi < a.Lq) {
-    E* row = (E*)a.dq + (((size_t)b * a.Lq + qi) * a.Hq + hq) * D;
-    const float sc = a.scale;
-#pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) {
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        *(uint2*)(row + 32 * dt + 8 * q4 + 4 * hh) =
-            make_uint2(pack2<TT>(dqacc[dt][4 * q4] * sc, dqacc[dt][4 * q4 + 1] * sc),
-                       pack2<TT>(dqacc[dt][4 * q4 + 2] * sc, dqacc[dt][4 * q4 + 3] * sc));
-      }
-    }
-  }
+  store_row16<TT, C::DT>((E*)a.dq + (((size_t)b * a.Lq + qi) * a.Hq + hq) * D, dqacc, a.scale, hh, qi < a.Lq);
 }
 
 template <typename TT, int D, bool DROP = false>
