@@ -260,7 +260,8 @@ int bwd_common(const void* q, const void* k, const void* v, const void* out, con
   if (q_empty && kv_empty) return ATTN_OK;  // nothing to write
   const size_t need = attn_bwd_workspace_size(B, Hq, Lq);
   if (need > 0 && (!workspace || !aligned(workspace, 16) || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
-  const int dev = check_device();
+  int cus = 0;
+  const int dev = check_device(&cus);
   if (dev != ATTN_OK) return dev;
 
   attn::BwdArgs a;
@@ -281,6 +282,9 @@ int bwd_common(const void* q, const void* k, const void* v, const void* out, con
   a.seed_lo = (uint32_t)seed;
   a.seed_hi = (uint32_t)(seed >> 32);
   a.drop_offset = offset;
+  // The dQ kernel's grid; at most one work-group per CU leaves each SIMD one
+  // wave, and the key-split instance then gives every work-group 8 waves.
+  a.kv_split = n_qblocks * Hq * (long long)B <= cus ? 1 : 0;
   hipError_t e = drop ? attn::launch_bwd_dropout(a, D, dtype, (hipStream_t)stream)
                       : attn::launch_bwd(a, D, dtype, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;

@@ -395,19 +395,28 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------------ dQ
 
-template <typename TT, int D, bool DROP>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
+// SPLIT (grids of at most one work-group per CU): 8 waves, two 4-wave halves
+// over alternate key tiles of the same 128 rows, each with its own tile
+// buffers; half 1 adds its dQ partial sums into half 0's through LDS at the
+// end.  Otherwise each work-group of 4 waves walks all tiles.
+template <typename TT, int D, bool DROP, bool SPLIT>
+__global__ __launch_bounds__(SPLIT ? 512 : 256, SPLIT ? 1 : 2) void bwd_dq_kernel(BwdArgs a) {
   using C = BwdCfg<D>;
   using E = typename TT::elem;
   using V8 = typename TT::vec8;
   using V4 = typename TT::vec4;
-  __shared__ __attribute__((aligned(16))) E kt0[C::TILE];
-  __shared__ __attribute__((aligned(16))) E kt1[C::TILE];
-  __shared__ __attribute__((aligned(16))) E vt0[C::TILE];
-  __shared__ __attribute__((aligned(16))) E vt1[C::TILE];
+  constexpr int NH = SPLIT ? 2 : 1;  // key halves
+  constexpr int TS = NH;             // tile stride of one half
+  __shared__ __attribute__((aligned(16))) E kt0[NH * C::TILE];
+  __shared__ __attribute__((aligned(16))) E kt1[NH * C::TILE];
+  __shared__ __attribute__((aligned(16))) E vt0[NH * C::TILE];
+  __shared__ __attribute__((aligned(16))) E vt1[NH * C::TILE];
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_id = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = wave_id & 3;               // 32-row group of the work-group's rows
+  const int hf = SPLIT ? (wave_id >> 2) : 0;  // key half
+  const int hoff = hf * C::TILE;              // this half's tile buffers
   const int hh = lane >> 5, l32 = lane & 31, j16 = lane & 15, grp = lane >> 4;
 
   const int n_heads = a.B * a.Hq;
@@ -462,14 +471,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 
   int noff[C::DSTEPS];
 #pragma unroll
-  for (int s = 0; s < C::DSTEPS; ++s) noff[s] = l32 * D + (((2 * s + hh) ^ bswz(l32)) << 3);
+  for (int s = 0; s < C::DSTEPS; ++s) noff[s] = hoff + l32 * D + (((2 * s + hh) ^ bswz(l32)) << 3);
   int toff[C::DT];
   {
     const int r = 4 * hh + (j16 >> 2);
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) {
       const int col = 32 * dt + 16 * (grp & 1) + 4 * (j16 & 3);
-      toff[dt] = r * D + ((((col >> 3) ^ bswz(r)) << 3) + 4 * ((col >> 2) & 1));
+      toff[dt] = hoff + r * D + ((((col >> 3) ^ bswz(r)) << 3) + 4 * ((col >> 2) & 1));
     }
   }
 
@@ -490,8 +499,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     const rsrc_t rv = make_rsrc(vb + (size_t)t * C::BN * kv_rs, bytes);
 #pragma unroll
     for (int i = 0; i < C::IPW; ++i) {
-      buf_load16_lds(rk, src[i], (P ? kt1 : kt0) + (wave * C::IPW + i) * C::RPI * D);
-      buf_load16_lds(rv, src[i], (P ? vt1 : vt0) + (wave * C::IPW + i) * C::RPI * D);
+      buf_load16_lds(rk, src[i], (P ? kt1 : kt0) + hoff + (wave * C::IPW + i) * C::RPI * D);
+      buf_load16_lds(rv, src[i], (P ? vt1 : vt0) + hoff + (wave * C::IPW + i) * C::RPI * D);
     }
   };
 
@@ -500,9 +509,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   for (int dt = 0; dt < C::DT; ++dt) dqacc[dt] = f32x16{};
   const float sl2 = a.scale_log2;
 
+  // (SPLIT: t+1 below is this half's next tile, t+2.  The next tile is
+  // issued even past the range, where it loads zeros: half 1's last body
+  // may be such a tile, and its buffer must not hold an older tile.)
   auto body = [&](int t, auto par) {
     constexpr int P = decltype(par)::value;
-    if (t + 1 < t_hi) issue(t + 1, Par<1 - P>{});
+    if (SPLIT || t + TS < t_hi) issue(t + TS, Par<1 - P>{});
     const E* ks = P ? kt1 : kt0;
     const E* vs = P ? vt1 : vt0;
     // S^T = K Q^T and dP^T = V dO^T: 64 keys (two halves) x 32 rows.
@@ -574,16 +586,55 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   };
 
   if (t_lo < t_hi) {
-    issue(t_lo, Par<0>{});
+    issue(t_lo + hf, Par<0>{});  // SPLIT: past the range (one tile) it loads zeros
     wait_vmem();
     __syncthreads();
-    for (int t = t_lo; t < t_hi; t += 2) {
-      body(t, Par<0>{});
-      if (t + 1 < t_hi) body(t + 1, Par<1>{});
+    // Both halves run the same number of bodies (the barriers are the
+    // work-group's); with an odd tile count half 1's last tile lies past the
+    // range, holds zeros and is masked whole, so it adds nothing.
+    const int n_it = (t_hi - t_lo + NH - 1) / NH;
+    for (int i = 0; i < n_it; i += 2) {
+      body(t_lo + hf + i * TS, Par<0>{});
+      if (i + 1 < n_it) body(t_lo + hf + (i + 1) * TS, Par<1>{});
     }
   }
 
-  store_row16<TT, C::DT>((E*)a.dq + (((size_t)b * a.Lq + qi) * a.Hq + hq) * D, dqacc, a.scale, hh, qi < a.Lq);
+  if constexpr (SPLIT) {
+    // Every load has landed and every wave passed the last barrier (or none
+    // ran), so the tile buffers are free: half 1 leaves its sums in them,
+    // lane for lane, and half 0 adds them.
+    __syncthreads();
+    float* xo[4] = {(float*)kt0, (float*)kt1, (float*)vt0, (float*)vt1};
+    const int xi = wave * 64 + lane;
+    if (hf == 1) {
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xo[dt][r * 256 + xi] = dqacc[dt][r];
+    }
+    __syncthreads();
+    if (hf == 1) return;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dqacc[dt][r] += xo[dt][r * 256 + xi];
+  }
+  E* dqrow = (E*)a.dq + (((size_t)b * a.Lq + qi) * a.Hq + hq) * D;
+  if constexpr (DROP) {
+    // The dropout instance has no registers to spare for the lane-pair swap
+    // of store_row16 (its D = 128 kernel would spill): 8-byte stores.
+    if (qi < a.Lq) {
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *(uint2*)(dqrow + 32 * dt + 8 * q4 + 4 * hh) =
+              make_uint2(pack2<TT>(dqacc[dt][4 * q4] * a.scale, dqacc[dt][4 * q4 + 1] * a.scale),
+                         pack2<TT>(dqacc[dt][4 * q4 + 2] * a.scale, dqacc[dt][4 * q4 + 3] * a.scale));
+    }
+  } else {
+    store_row16<TT, C::DT>(dqrow, dqacc, a.scale, hh, qi < a.Lq);
+  }
 }
 
 template <typename TT, int D, bool DROP = false>
@@ -605,7 +656,10 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   }
   const long long qblocks = (long long)a.n_qblocks * a.B * a.Hq;
   if (qblocks > 0) {
-    hipLaunchKernelGGL((bwd_dq_kernel<TT, D, DROP>), dim3((unsigned)qblocks), dim3(256), 0, stream, a);
+    if (a.kv_split)
+      hipLaunchKernelGGL((bwd_dq_kernel<TT, D, DROP, true>), dim3((unsigned)qblocks), dim3(512), 0, stream, a);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<TT, D, DROP, false>), dim3((unsigned)qblocks), dim3(256), 0, stream, a);
     e = hipGetLastError();
   }
   return e;

@@ -235,9 +235,10 @@ __device__ __forceinline__ uint32_t pack2<F16>(float a, float b) {
 // The swaps run in every lane; store selects the lanes that write.
 template <typename TT, int DB>
 __device__ __forceinline__ void store_row16(void* orow, const f32x16 (&acc)[DB], float inv, int hh, bool store) {
-  uint4 w[DB][2];
+  uint16_t* o = (uint16_t*)orow;  // 16-bit elements
 #pragma unroll
-  for (int d = 0; d < DB; ++d) {
+  for (int d = 0; d < DB; ++d) {  // one block at a time: few extra registers live
+    uint4 w[2];
 #pragma unroll
     for (int qp = 0; qp < 2; ++qp) {
       uint32_t e[2][2];  // [q = 2*qp + i][dword]
@@ -249,15 +250,12 @@ __device__ __forceinline__ void store_row16(void* orow, const f32x16 (&acc)[DB],
       }
       const auto x = __builtin_amdgcn_permlane32_swap(e[0][0], e[1][0], false, false);
       const auto y = __builtin_amdgcn_permlane32_swap(e[0][1], e[1][1], false, false);
-      w[d][qp] = make_uint4(x[0], y[0], x[1], y[1]);
+      w[qp] = make_uint4(x[0], y[0], x[1], y[1]);
     }
-  }
-  if (store) {
-    uint16_t* o = (uint16_t*)orow;  // 16-bit elements
+    if (store) {
 #pragma unroll
-    for (int d = 0; d < DB; ++d)
-#pragma unroll
-      for (int qp = 0; qp < 2; ++qp) *(uint4*)(o + 32 * d + 16 * qp + 8 * hh) = w[d][qp];
+      for (int qp = 0; qp < 2; ++qp) *(uint4*)(o + 32 * d + 16 * qp + 8 * hh) = w[qp];
+    }
   }
 }
 

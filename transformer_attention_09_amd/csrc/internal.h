@@ -84,6 +84,9 @@ struct BwdArgs {
   // with the same Philox counter, key and threshold as FwdArgs.
   uint32_t drop_thr, seed_lo, seed_hi, drop_offset;
   float drop_scale;
+  // The dQ kernel splits each work-group's key tiles between two 4-wave
+  // halves (set when its grid has no more work-groups than the device has CUs).
+  int kv_split;
 };
 
 // FP8 forward: q, k, v e4m3 (OCP float8_e4m3fn), out bf16; scale_log2 holds
