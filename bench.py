@@ -158,14 +158,36 @@ def write_traffic_record(fetch_csv, write_csv, command):
     print("\n".join(out))
 
 
-def cpu_baseline(cfg, target_s=20.0):
-    """The fp64 oracle, as it stands, on a bounded sample of the same forward
-    workload: every query head, a strided subset of query rows."""
+def host_cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None if unreadable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(cfg, dcfg, target_s=15.0):
+    """The fp64 oracle, as it stands, timed on this host's cores.
+
+    Forward: a bounded sample of the same workload (every query head, an
+    evenly spaced subset of query rows sized to about target_s seconds), flops
+    counted as for the GPU.  Decode: the whole paged-decode workload, bytes
+    counted as for the GPU.  BLAS (the only multi-threaded part of the oracle)
+    runs on as many threads as this process may use: the CPUs in its affinity
+    mask, capped by OMP_NUM_THREADS when that is set."""
     import numpy as np
     import threadpoolctl
 
     import oracle
-    from workloads import dense_inputs
+    from workloads import dense_inputs, paged_inputs
+
+    affinity = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS")
+    threads = min(affinity, int(cap)) if cap and cap.isdigit() and int(cap) > 0 else affinity
 
     q, k, v = dense_inputs(cfg)
     q64, k64, v64 = (t.double().numpy() for t in (q, k, v))
@@ -180,17 +202,26 @@ def cpu_baseline(cfg, target_s=20.0):
         vis = np.minimum(i, cfg.Lk - 1) + 1 if cfg.causal else np.full(len(rows), cfg.Lk)
         return 4.0 * cfg.B * cfg.Hq * cfg.D * float(vis.sum())
 
-    probe = np.arange(0, cfg.Lq, cfg.Lq // 64)
-    t_probe = run(probe)
-    n = int(min(cfg.Lq, max(64, len(probe) * target_s / max(t_probe, 1e-3))))
-    rows = np.unique(np.linspace(0, cfg.Lq - 1, n).astype(np.int64))
-    t = run(rows)
-    info = threadpoolctl.threadpool_info()
-    cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
-    return {"value": flops(rows) / t / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+    pin = paged_inputs(dcfg)
+    with threadpoolctl.threadpool_limits(threads):
+        probe = np.arange(0, cfg.Lq, cfg.Lq // 64)
+        t_probe = run(probe)
+        n = int(min(cfg.Lq, max(64, len(probe) * target_s / max(t_probe, 1e-3))))
+        rows = np.unique(np.linspace(0, cfg.Lq - 1, n).astype(np.int64))
+        t = run(rows)
+        t0 = time.perf_counter()
+        oracle.decode_paged(pin.q, pin.k_cache, pin.v_cache, pin.block_table, pin.ctx_lens, dcfg.block_size,
+                            dcfg.scale)
+        t_dec = time.perf_counter() - t0
+    d_bytes = decode_bytes(pin.ctx_lens.numpy(), dcfg.Hq, dcfg.Hkv, dcfg.D)
+    return {"value": flops(rows) / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{cfg.name}: {len(rows)} of {cfg.Lq} query rows (evenly spaced), all {cfg.Hq} heads, "
                       f"{t:.1f} s; flops counted as for the GPU (visible keys only)",
-            "seconds": t}
+            "seconds": t,
+            "affinity_cpus": affinity,
+            "cpu_model": host_cpu_model(),
+            "decode": {"value": d_bytes / t_dec / 1e9, "unit": "GB/s", "seconds": t_dec,
+                       "sample": f"{dcfg.name}: all {dcfg.num_seqs} sequences, bytes counted as for the GPU"}}
 
 
 def read_ceiling(ta, torch, dev, stream, nbytes=2 << 30, reps=5):
@@ -586,7 +617,7 @@ def main():
 
     if not args.no_cpu:
         log("timing the CPU oracle on a sample ...")
-        result["cpu_baseline"] = cpu_baseline(fcfg)
+        result["cpu_baseline"] = cpu_baseline(fcfg, CONFIGS["paged_decode"])
         log(f"cpu baseline: {result['cpu_baseline']}")
     else:
         result["cpu_baseline"] = None

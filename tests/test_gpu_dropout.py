@@ -137,7 +137,9 @@ def test_dropout_workloads_sampled_rows(gpu_lib, name, p):
     say(f"[case] dropout workload {name} p{p} (sampled rows)")
     q, k, v = dense_inputs(cfg)
     out, lse = run_drop(gpu_lib, q, k, v, p, 77, 1, cfg.scale, cfg.causal, cfg.window)
-    rows = np.unique(np.concatenate([np.arange(0, 40), np.linspace(0, cfg.Lq - 1, 24).astype(np.int64),
+    # one row from every 32-row wave group of every q-block, plus both ends
+    per_group = np.arange(0, cfg.Lq, 32) + np.random.default_rng(cfg.seed).integers(0, 32, size=-(-cfg.Lq // 32))
+    rows = np.unique(np.concatenate([np.arange(0, 40), np.minimum(per_group, cfg.Lq - 1),
                                      np.arange(cfg.Lq - 40, cfg.Lq)]))
     check_out(name, out, lse, q, k, v, cfg.scale, cfg.causal, cfg.window, p, 77, 1, cfg.dtype, rows=rows)
 

@@ -65,11 +65,6 @@ struct BwdCfg {
 // fixed +8 and +16 row steps on the same chunk pattern.
 __device__ __forceinline__ int bswz(int r) { return r & 7; }
 
-// A buffer resource's byte range, saturated to what the 32-bit field holds.
-__device__ __forceinline__ uint32_t range32(size_t bytes) {
-  return bytes > 0x7fffffffu ? 0x7fffffffu : (uint32_t)bytes;
-}
-
 // ------------------------------------------------------------------ preprocess
 
 template <typename TT, int D>
@@ -149,7 +144,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // each wave reads its 32 keys' rows as B operands (k over the head dim).
   const size_t kv_rs = (size_t)a.Hkv * D;
   {
-    const uint32_t bytes = k0 < a.Lk ? range32((((size_t)(a.Lk - k0) - 1) * kv_rs + D) * sizeof(E)) : 0u;
+    const uint32_t bytes = rows_range((long long)a.Lk - k0, kv_rs, D, sizeof(E));
     const rsrc_t rk = make_rsrc((const E*)a.k + ((size_t)b * a.Lk + k0) * kv_rs + (size_t)g * D, bytes);
     const rsrc_t rv = make_rsrc((const E*)a.v + ((size_t)b * a.Lk + k0) * kv_rs + (size_t)g * D, bytes);
     constexpr int IPB = C::BK / C::RPI / 8;  // load instructions per wave for 128 rows
@@ -194,7 +189,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
     constexpr int P = decltype(par)::value;
     const int h = g * a.group + it / nq;
     const int i0 = (qt_lo + it % nq) * C::BQ;
-    const uint32_t bytes = range32((((size_t)(a.Lq - i0) - 1) * a.Hq * D + D) * sizeof(E));
+    const uint32_t bytes = rows_range((long long)a.Lq - i0, (size_t)a.Hq * D, D, sizeof(E));
     const size_t base = (((size_t)b * a.Lq + i0) * a.Hq + h) * D;
     const rsrc_t rq = make_rsrc((const E*)a.q + base, bytes);
     const rsrc_t rg = make_rsrc((const E*)a.dout + base, bytes);
@@ -453,7 +448,7 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256, SPLIT ? 1 : 2) void bwd_dq_kerne
   float l2 = INFINITY, dvv = 0.f;
   {
     const size_t base = (((size_t)b * a.Lq + q0) * a.Hq + hq) * D;
-    const uint32_t bytes = range32((((size_t)(a.Lq - q0) - 1) * a.Hq * D + D) * sizeof(E));
+    const uint32_t bytes = rows_range((long long)a.Lq - q0, (size_t)a.Hq * D, D, sizeof(E));
     const rsrc_t rq = make_rsrc((const E*)a.q + base, bytes);
     const rsrc_t rg = make_rsrc((const E*)a.dout + base, bytes);
     const uint32_t o = (uint32_t)(((size_t)(wave * 32 + l32) * a.Hq * D + 8 * hh) * sizeof(E));
@@ -494,7 +489,7 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256, SPLIT ? 1 : 2) void bwd_dq_kerne
   }
   auto issue = [&](int t, auto par) {
     constexpr int P = decltype(par)::value;
-    const uint32_t bytes = t < t_hi ? range32((((size_t)(a.Lk - t * C::BN) - 1) * kv_rs + D) * sizeof(E)) : 0u;
+    const uint32_t bytes = t < t_hi ? rows_range((long long)a.Lk - (long long)t * C::BN, kv_rs, D, sizeof(E)) : 0u;
     const rsrc_t rk = make_rsrc(kb + (size_t)t * C::BN * kv_rs, bytes);
     const rsrc_t rv = make_rsrc(vb + (size_t)t * C::BN * kv_rs, bytes);
 #pragma unroll

@@ -18,6 +18,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "ranges.h"
+
 #include <type_traits>
 #include <utility>
 

@@ -232,7 +232,7 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256, SPLIT ? 1 : 2) void fwd_kernel(F
     // Rows q0.. of this head: row i at (i - q0) * Hq * D elements; rows past
     // Lq read as zeros through the resource range.
     const E* qbase = (const E*)a.q + ((size_t)((size_t)b * a.Lq + q0) * a.Hq + hq) * D;
-    const rsrc_t qr = make_rsrc(qbase, (uint32_t)(((size_t)(a.Lq - q0 - 1) * a.Hq + 1) * D * sizeof(E)));
+    const rsrc_t qr = make_rsrc(qbase, rows_range(a.Lq - q0, (size_t)a.Hq * D, D, sizeof(E)));
     const uint32_t qo = (uint32_t)(((size_t)(wave * 32 + l32) * a.Hq * D + 8 * hh) * sizeof(E));
 #pragma unroll
     for (int s = 0; s < C::KSTEPS; ++s) {
@@ -303,9 +303,7 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256, SPLIT ? 1 : 2) void fwd_kernel(F
     // rows past the end of the keys load as zeros; tiles past the range get
     // an empty resource (the loads then only write zeros to a free buffer).
     if (t >= t_hi) return 0u;
-    const size_t jt = (size_t)t * C::BN;
-    const size_t bytes = (((size_t)(Lk - jt) - 1) * kv_rs + D) * sizeof(E);
-    return bytes > 0x7fffffffu ? 0x7fffffffu : (uint32_t)bytes;
+    return rows_range((long long)Lk - (long long)t * C::BN, kv_rs, D, sizeof(E));
   };
   // Paged: the table row of sequence b (entries past its end read as 0) and
   // the resource of this wave's block of tile t.  A block holding no visible

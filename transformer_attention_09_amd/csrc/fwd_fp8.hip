@@ -114,8 +114,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(F8Args a) {
   i32x8 qf[C::KS];
   {
     const size_t base = (((size_t)b * a.Lq + q0) * a.Hq + hq) * D;
-    const size_t by = ((size_t)(a.Lq - q0) - 1) * a.Hq * D + D;
-    const rsrc_t rq = make_rsrc((const unsigned char*)a.q + base, by > 0x7fffffffu ? 0x7fffffffu : (uint32_t)by);
+    const rsrc_t rq = make_rsrc((const unsigned char*)a.q + base, rows_range(a.Lq - q0, (size_t)a.Hq * D, D, 1));
     const uint32_t o = (uint32_t)((size_t)(wave * 32 + l32) * a.Hq * D + 32 * hh);
 #pragma unroll
     for (int s = 0; s < C::KS; ++s) {
@@ -157,11 +156,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(F8Args a) {
   }
   auto issue = [&](int t, auto par) {
     constexpr int P = decltype(par)::value;
-    uint32_t bytes = 0u;
-    if (t < t_hi) {
-      const size_t by = ((size_t)(a.Lk - t * C::BN) - 1) * row_bytes + D;
-      bytes = by > 0x7fffffffu ? 0x7fffffffu : (uint32_t)by;
-    }
+    const uint32_t bytes = t < t_hi ? rows_range((long long)a.Lk - (long long)t * C::BN, row_bytes, D, 1) : 0u;
     const rsrc_t rk = make_rsrc(kb + (size_t)t * C::BN * row_bytes, bytes);
     const rsrc_t rv = make_rsrc(vb + (size_t)t * C::BN * row_bytes, bytes);
 #pragma unroll
