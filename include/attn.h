@@ -60,7 +60,9 @@ enum {
   ATTN_ERR_ALIGN = -4,       /* a tensor pointer is not suitably aligned          */
   ATTN_ERR_WORKSPACE = -5,   /* decode workspace missing, misaligned or too small  */
   ATTN_ERR_DEVICE = -6,      /* no current HIP device, or it is not gfx950         */
-  ATTN_ERR_HIP = -7          /* the HIP runtime reported an error at launch        */
+  ATTN_ERR_HIP = -7,         /* the HIP runtime reported an error at launch        */
+  ATTN_ERR_SCRATCH = -8      /* attn_decode_paged_static: the call needs more than
+                                the library's static scratch holds                */
 };
 
 /*
@@ -154,6 +156,35 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                       void* out, float* lse,
                       int num_seqs, int Hq, int Hkv, int D, int max_blocks_per_seq, int num_blocks,
                       float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode_paged_static - attn_decode_paged without a caller workspace and
+ * without any allocation, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).
+ *
+ * Arguments, layouts, preconditions and results are those of
+ * attn_decode_paged (the same kernels run, so outputs are bit-identical); the
+ * partial results between its two kernels live instead in a static device
+ * array of ATTN_DECODE_STATIC_SCRATCH_BYTES that the library holds on every
+ * device it runs on until the process ends.  A call needs
+ * (R + min(num_seqs, 2048)) * Hq * (D + 1) * 4 bytes of it, where R, the
+ * number of ranges per KV head, is at most 4 * (CU count) / Hkv (512 for
+ * Hkv = 2 on a 256-CU device): 3.6 MB for 64 sequences with Hq = 12,
+ * D = 128; larger calls return ATTN_ERR_SCRATCH and launch nothing.
+ * Every call on one device shares that device's array: calls that overlap in
+ * time on one device (different streams, or different host threads without
+ * ordering) race and give unspecified results; calls ordered on one stream
+ * are safe.  Nothing in the array needs clearing between calls.
+ * Errors: those of attn_decode_paged except ATTN_ERR_WORKSPACE, plus
+ * ATTN_ERR_SCRATCH.
+ */
+#define ATTN_DECODE_STATIC_SCRATCH_BYTES (16u << 20)
+int attn_decode_paged_static(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_table, const int32_t* ctx_lens, int block_size,
+                             void* out, float* lse,
+                             int num_seqs, int Hq, int Hkv, int D, int max_blocks_per_seq, int num_blocks,
+                             float scale, int dtype, void* stream);
 
 /*
  * attn_fwd_paged - fused attention forward for Lq new query tokens per

@@ -7,6 +7,7 @@ the C ABI declared in include/attn.h, with the same entry-point names:
     attn_fwd(q, k, v, ...)                  q [B,Lq,Hq,D], k/v [B,Lk,Hkv,D]
     attn_fwd_dropout(q, k, v, p, seed, ...) the same with dropout on the probabilities
     attn_decode_paged(q, k_cache, ...)      q [S,Hq,D], caches [N,16,Hkv,D]
+    attn_decode_paged_static(q, k_cache, ...)  the same without a workspace (no allocation)
     attn_fwd_paged(q, k_cache, ...)         q [B,Lq,Hq,D] over paged caches [N,16,Hkv,D]
     attn_bwd(q, k, v, out, dout, lse, ...)  gradients dq, dk, dv
     attn_bwd_dropout(..., p, seed, ...)     gradients of attn_fwd_dropout's output
@@ -40,10 +41,11 @@ STATUS = {
     -5: "ATTN_ERR_WORKSPACE",
     -6: "ATTN_ERR_DEVICE",
     -7: "ATTN_ERR_HIP",
+    -8: "ATTN_ERR_SCRATCH",
 }
 EXPORTED = ("attn_fwd", "attn_decode_paged", "attn_decode_paged_workspace_size", "attn_status_string",
             "attn_fwd_paged", "attn_bwd", "attn_bwd_workspace_size", "attn_fwd_fp8", "attn_hbm_read_probe",
-            "attn_fwd_dropout", "attn_bwd_dropout")
+            "attn_fwd_dropout", "attn_bwd_dropout", "attn_decode_paged_static")
 
 _lib = None
 _lock = threading.Lock()
@@ -70,6 +72,9 @@ def load_library() -> ctypes.CDLL:
             lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
                                               f32, i32, vp, sz, vp]
             lib.attn_decode_paged.restype = i32
+            lib.attn_decode_paged_static.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
+                                                     i32, f32, i32, vp]
+            lib.attn_decode_paged_static.restype = i32
             lib.attn_decode_paged_workspace_size.argtypes = [i32, i32, i32, i32, i32]
             lib.attn_decode_paged_workspace_size.restype = sz
             lib.attn_status_string.argtypes = [i32]
@@ -258,6 +263,35 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, ctx_lens, out=None, lse=
                                           ws_ptr, ws_bytes, _stream_handle(stream))
     if st != 0:
         raise AttnError(st, "attn_decode_paged")
+    return out, lse
+
+
+def attn_decode_paged_static(q, k_cache, v_cache, block_table, ctx_lens, out, lse=None,
+                             scale: Optional[float] = None, stream=None):
+    """Paged-KV decode that allocates nothing: the caller passes out (and lse,
+    optional) and the library keeps its partial results in a static device
+    array (attn_decode_paged_static in include/attn.h).  Calls that overlap in
+    time on one device race; calls ordered on one stream do not."""
+    for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("block_table", block_table),
+                 ("ctx_lens", ctx_lens), ("out", out)):
+        _require_cuda(n, t)
+    if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape or out.shape != q.shape:
+        raise ValueError("expected q, out [S,Hq,D] and caches [N,block_size,Hkv,D] of equal shape")
+    S, Hq, D = q.shape
+    num_blocks, bs, Hkv, Dk = k_cache.shape
+    if Dk != D or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype or out.dtype != q.dtype:
+        raise ValueError("q, out and caches disagree in head dim or dtype")
+    if block_table.dim() != 2 or block_table.shape[0] != S or ctx_lens.shape != (S,):
+        raise ValueError("block_table must be [S, max_blocks_per_seq] and ctx_lens [S]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    st = load_library().attn_decode_paged_static(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                                 block_table.data_ptr(), ctx_lens.data_ptr(), bs,
+                                                 out.data_ptr(), lse.data_ptr() if lse is not None else None,
+                                                 S, Hq, Hkv, D, block_table.shape[1], num_blocks, float(scale),
+                                                 _dtype_code(q), _stream_handle(stream))
+    if st != 0:
+        raise AttnError(st, "attn_decode_paged_static")
     return out, lse
 
 

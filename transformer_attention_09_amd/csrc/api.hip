@@ -75,6 +75,7 @@ ATTN_API const char* attn_status_string(int status) {
     case ATTN_ERR_WORKSPACE: return "decode workspace missing, misaligned or too small";
     case ATTN_ERR_DEVICE: return "no current HIP device, or it is not gfx950";
     case ATTN_ERR_HIP: return "HIP runtime error at launch";
+    case ATTN_ERR_SCRATCH: return "the call needs more than the library's static decode scratch holds";
     default: return "unknown status";
   }
 }
@@ -328,12 +329,12 @@ ATTN_API size_t attn_decode_paged_workspace_size(int num_seqs, int Hq, int D, in
   return (size_t)slots * Hq * (D + 1) * sizeof(float);
 }
 
-ATTN_API int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
-                               const int32_t* block_table, const int32_t* ctx_lens, int block_size,
-                               void* out, float* lse,
-                               int num_seqs, int Hq, int Hkv, int D, int max_blocks_per_seq, int num_blocks,
-                               float scale, int dtype, void* workspace, size_t workspace_bytes,
-                               void* stream) {
+namespace {
+
+// Host checks shared by the decode entry points (everything but the workspace).
+int decode_validate(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                    const int32_t* ctx_lens, int block_size, void* out, float* lse, int num_seqs, int Hq, int Hkv,
+                    int D, int max_blocks_per_seq, int num_blocks, float scale, int dtype) {
   if (num_seqs < 0 || Hq <= 0 || Hkv <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0) return ATTN_ERR_SHAPE;
   if (num_seqs > 0 && (!q || !k_cache || !v_cache || !block_table || !ctx_lens || !out)) return ATTN_ERR_NULL;
   if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
@@ -347,31 +348,34 @@ ATTN_API int attn_decode_paged(const void* q, const void* k_cache, const void* v
       !aligned(block_table, 4) || !aligned(ctx_lens, 4))
     return ATTN_ERR_ALIGN;
   if (lse && !aligned(lse, 4)) return ATTN_ERR_ALIGN;
-  if (num_seqs == 0) return ATTN_OK;
-  const size_t need = attn_decode_paged_workspace_size(num_seqs, Hq, D, max_blocks_per_seq, block_size);
-  if (need == 0 || !workspace || workspace_bytes < need || !aligned(workspace, 16)) return ATTN_ERR_WORKSPACE;
-  const int group = Hq / Hkv;
-  const int n_hgroups = (group + 15) / 16;
-  int cus = 0;
-  const int dev = check_device(&cus);
-  if (dev != ATTN_OK) return dev;
+  return ATTN_OK;
+}
 
+// Ranges per (KV head, head group) of one decode launch: enough waves to give
+// every CU one resident work-group, never more ranges than blocks.
+long long decode_streams(int cus, int Hkv, int n_hgroups, int num_seqs, int max_blocks_per_seq) {
   const int per_launch = decode_seqs_per_launch(max_blocks_per_seq);
-  // Ranges per (KV head, head group): enough waves to give every CU one
-  // resident work-group, never more ranges than blocks.
   long long streams = (long long)cus * attn::kDecodeWavesPerCU / ((long long)Hkv * n_hgroups);
   streams = std::min<long long>(streams, (long long)std::min(num_seqs, per_launch) * max_blocks_per_seq);
-  streams = std::max<long long>(1, std::min<long long>(streams, attn::kDecodeMaxStreams));
-  const size_t esz = 2;  // fp16 / bf16
-  const size_t slots = (size_t)decode_slots(num_seqs, max_blocks_per_seq);
+  return std::max<long long>(1, std::min<long long>(streams, attn::kDecodeMaxStreams));
+}
 
+// Launches of the decode over `workspace`, laid out as `slots` partial
+// outputs [slots, Hq, D] followed by their log2-sum-exps [slots, Hq].
+int decode_launch(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                  const int32_t* ctx_lens, void* out, float* lse, int num_seqs, int Hq, int Hkv, int D,
+                  int max_blocks_per_seq, int num_blocks, float scale, int dtype, float* workspace, size_t slots,
+                  long long streams, void* stream) {
+  const int group = Hq / Hkv;
+  const int per_launch = decode_seqs_per_launch(max_blocks_per_seq);
+  const size_t esz = 2;  // fp16 / bf16
   attn::DecArgs a;
   a.k_cache = k_cache; a.v_cache = v_cache;
-  a.ws_o = (float*)workspace;
-  a.ws_lse = (float*)workspace + slots * Hq * D;
+  a.ws_o = workspace;
+  a.ws_lse = workspace + slots * Hq * D;
   a.Hq = Hq; a.Hkv = Hkv; a.group = group;
   a.max_blocks_per_seq = max_blocks_per_seq; a.num_blocks = num_blocks;
-  a.n_hgroups = n_hgroups;
+  a.n_hgroups = (group + 15) / 16;
   a.streams = (int)streams;
   a.scale_log2 = scale * attn::kLog2e;
   // Launches of successive sequence batches share the workspace; the stream
@@ -388,6 +392,84 @@ ATTN_API int attn_decode_paged(const void* q, const void* k_cache, const void* v
     if (e != hipSuccess) return ATTN_ERR_HIP;
   }
   return ATTN_OK;
+}
+
+}  // namespace
+
+ATTN_API int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_table, const int32_t* ctx_lens, int block_size,
+                               void* out, float* lse,
+                               int num_seqs, int Hq, int Hkv, int D, int max_blocks_per_seq, int num_blocks,
+                               float scale, int dtype, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  const int v = decode_validate(q, k_cache, v_cache, block_table, ctx_lens, block_size, out, lse, num_seqs, Hq,
+                                Hkv, D, max_blocks_per_seq, num_blocks, scale, dtype);
+  if (v != ATTN_OK) return v;
+  if (num_seqs == 0) return ATTN_OK;
+  const size_t need = attn_decode_paged_workspace_size(num_seqs, Hq, D, max_blocks_per_seq, block_size);
+  if (need == 0 || !workspace || workspace_bytes < need || !aligned(workspace, 16)) return ATTN_ERR_WORKSPACE;
+  int cus = 0;
+  const int dev = check_device(&cus);
+  if (dev != ATTN_OK) return dev;
+  const long long streams = decode_streams(cus, Hkv, (Hq / Hkv + 15) / 16, num_seqs, max_blocks_per_seq);
+  return decode_launch(q, k_cache, v_cache, block_table, ctx_lens, out, lse, num_seqs, Hq, Hkv, D,
+                       max_blocks_per_seq, num_blocks, scale, dtype, (float*)workspace,
+                       (size_t)decode_slots(num_seqs, max_blocks_per_seq), streams, stream);
+}
+
+// ---------------------------------------------------------------- no-alloc decode
+//
+// attn_decode_paged_static keeps the decode's partial results in `scratch`, a
+// static device array of ATTN_DECODE_STATIC_SCRATCH_BYTES that every device
+// the library runs on holds until the process ends.  On the host the array's
+// name is only a stand-in for the device address, so its address on each
+// device is looked up once (with that device current) and only that pointer
+// is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[ATTN_DECODE_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+std::atomic<void*> g_scratch[kMaxDevices];
+
+// This device's address of `scratch` (nullptr if the lookup fails).  Racing
+// first calls on one device both look it up and store the same value.
+void* scratch_ptr(int dev) {
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    void* found = nullptr;
+    if (hipGetSymbolAddress(&found, HIP_SYMBOL(scratch)) != hipSuccess || found == nullptr) return nullptr;
+    g_scratch[dev].store(found, std::memory_order_release);
+    p = found;
+  }
+  return p;
+}
+
+}  // namespace
+
+ATTN_API int attn_decode_paged_static(const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_table, const int32_t* ctx_lens, int block_size,
+                                      void* out, float* lse,
+                                      int num_seqs, int Hq, int Hkv, int D, int max_blocks_per_seq,
+                                      int num_blocks, float scale, int dtype, void* stream) {
+  const int v = decode_validate(q, k_cache, v_cache, block_table, ctx_lens, block_size, out, lse, num_seqs, Hq,
+                                Hkv, D, max_blocks_per_seq, num_blocks, scale, dtype);
+  if (v != ATTN_OK) return v;
+  if (num_seqs == 0) return ATTN_OK;
+  int cus = 0;
+  const int st = check_device(&cus);
+  if (st != ATTN_OK) return st;
+  // Slots actually addressed: range index + sequence index of one launch.
+  const long long streams = decode_streams(cus, Hkv, (Hq / Hkv + 15) / 16, num_seqs, max_blocks_per_seq);
+  const long long slots = streams + std::min(num_seqs, decode_seqs_per_launch(max_blocks_per_seq));
+  if (!prod_ok(slots, Hq, D + 1, (long long)sizeof(float)) ||
+      slots * Hq * (D + 1) * (long long)sizeof(float) > (long long)ATTN_DECODE_STATIC_SCRATCH_BYTES)
+    return ATTN_ERR_SCRATCH;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ATTN_ERR_DEVICE;
+  void* ws = scratch_ptr(dev);
+  if (ws == nullptr) return ATTN_ERR_HIP;
+  return decode_launch(q, k_cache, v_cache, block_table, ctx_lens, out, lse, num_seqs, Hq, Hkv, D,
+                       max_blocks_per_seq, num_blocks, scale, dtype, (float*)ws, (size_t)slots, streams, stream);
 }
 
 ATTN_API int attn_hbm_read_probe(const void* p, size_t bytes, unsigned int* sink, void* stream) {
