@@ -15,9 +15,13 @@ events, with the per-call figure inside the step loop shown too.  The decode
 rotates through KV-pool replicas totalling >= 1 GiB so no timed call finds
 its K/V in the 256 MB last-level cache.
 
-The decode is also compared with a plain streaming read of 2 GiB on the same
-device (attn_hbm_read_probe), the attainable HBM rate, and the shader clock is
-sampled with rocm-smi while a batch of forward launches runs.
+Before the W warmup steps, untimed steps run for one second so that the timed
+ones see the shader clock it settles to under sustained load.  The decode is
+also compared with a plain streaming read on the same device
+(attn_hbm_read_probe, the attainable HBM rate) of its own size, rotated over
+2 GiB, and of 2 GiB; the shader clock is sampled with rocm-smi while a batch of
+forward launches runs.  The per-workload detail times each forward over input
+replicas totalling at least 1 GiB (up to 64), one per launch in turn.
 
     python bench.py [--gpus 1] [--steps K=100] [--warmup W=10] [--no-cpu] [--no-detail]
 
@@ -42,6 +46,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, published
 KV_ROTATION_BYTES = 1 << 30
+SETTLE_S = 1.0              # untimed steps before the warmup: the shader clock settles under sustained load
 
 
 def log(*a):
@@ -224,22 +229,29 @@ def cpu_baseline(cfg, dcfg, target_s=15.0):
                        "sample": f"{dcfg.name}: all {dcfg.num_seqs} sequences, bytes counted as for the GPU"}}
 
 
-def read_ceiling(ta, torch, dev, stream, nbytes=2 << 30, reps=5):
-    """Attainable HBM read rate on this device: one plain streaming read of a
-    2 GiB buffer (attn_hbm_read_probe), averaged over a few back-to-back runs."""
+def read_ceiling(ta, torch, dev, stream, nbytes=2 << 30, reps=5, piece=None):
+    """Attainable HBM read rate on this device: plain streaming reads
+    (attn_hbm_read_probe) of a 2 GiB buffer, averaged over a few back-to-back
+    runs; with `piece`, reads of `piece` bytes each, rotating over the pieces
+    of the buffer so that no read finds its data in the 256 MB last-level
+    cache (the decode's own size and rotation)."""
     buf = torch.ones(nbytes, dtype=torch.uint8, device=dev)
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
-    for _ in range(2):
-        ta.attn_hbm_read_probe(buf, sink, stream=stream)
+    size = nbytes if piece is None else (piece // 16) * 16
+    parts = [buf[i * size:(i + 1) * size] for i in range(nbytes // size)]
+    n = len(parts) * (1 if piece is None else 4)
+    reps = reps if piece is None else max(reps, n)
+    for i in range(2):
+        ta.attn_hbm_read_probe(parts[i % len(parts)], sink, stream=stream)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    for _ in range(reps):
-        ta.attn_hbm_read_probe(buf, sink, stream=stream)
+    for i in range(reps):
+        ta.attn_hbm_read_probe(parts[i % len(parts)], sink, stream=stream)
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
-    del buf
-    return nbytes / (ms * 1e-3) / 1e9
+    del parts, buf
+    return size / (ms * 1e-3) / 1e9
 
 
 def under_profiler() -> bool:
@@ -341,15 +353,24 @@ def main():
         if ev is not None:
             ev[2].record(stream)
 
+    # The shader clock under sustained MFMA load takes a few hundred
+    # milliseconds to settle (the first launches of a run are the slowest), so
+    # untimed steps run for SETTLE_S seconds before the W warmup steps.
+    t_settle, n_settle = time.perf_counter(), 0
+    while time.perf_counter() - t_settle < SETTLE_S:
+        for _ in range(25):
+            step(n_settle)
+            n_settle += 1
+        torch.cuda.synchronize()
     for i in range(args.warmup):
-        step(i)
+        step(n_settle + i)
     torch.cuda.synchronize()
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        step(n_settle + args.warmup + i, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     f_all = [e[0].elapsed_time(e[1]) for e in evs]
@@ -393,8 +414,10 @@ def main():
 
     sclk = sclk_under_load(fwd_batch)
     torch.cuda.synchronize()
-    ceiling = read_ceiling(ta, torch, dev, stream)
-    log(f"plain streaming read of 2 GiB: {ceiling:.0f} GB/s; shader clock under forward load: {sclk} MHz")
+    ceiling_2g = read_ceiling(ta, torch, dev, stream)
+    ceiling = read_ceiling(ta, torch, dev, stream, piece=int(d_bytes))
+    log(f"plain streaming read: {ceiling:.0f} GB/s at the decode's size ({d_bytes / 1e6:.0f} MB per read, "
+        f"rotated over 2 GiB), {ceiling_2g:.0f} GB/s over 2 GiB; shader clock under forward load: {sclk} MHz")
     traffic = None
     if trec is not None and trec.get("workload") == fcfg.name:
         traffic = trec["fetch_bytes"] + trec["write_bytes"]
@@ -430,6 +453,7 @@ def main():
             "avg_launch_us": round(f_ms * 1e3, 2),
             "median_launch_us": round(f_med * 1e3, 2),
             "sclk_mhz_under_load": sclk,
+            "settle_steps": n_settle,
         },
         "decode": {
             "value": round(d_gbs, 1),
@@ -443,6 +467,7 @@ def main():
             "in_step_median_call_us": round(d_step_med * 1e3, 2),
             "kv_replicas": n_rep,
             "read_ceiling_GBs": round(ceiling, 1),
+            "read_ceiling_2GiB_GBs": round(ceiling_2g, 1),
             "frac_of_read_ceiling": round(d_gbs / ceiling, 4),
         },
     }
@@ -451,23 +476,37 @@ def main():
         detail = {}
 
         def time_fwd(cfg, iters=10):
-            qq, kk, vv = (t.to(dev) for t in dense_inputs(cfg))
-            for _ in range(3):
-                ta.attn_fwd(qq, kk, vv, scale=cfg.scale, causal=cfg.causal, window=cfg.window, stream=stream)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            o = torch.empty_like(qq)
-            l = torch.empty((cfg.B, cfg.Hq, cfg.Lq), dtype=torch.float32, device=dev)
-            e0.record(stream)
-            for _ in range(iters):
+            """Average launch time over input replicas totalling >= 1 GiB (at
+            most 64 replicas), one replica per launch in turn, so that a
+            launch whose inputs fit the 256 MB last-level cache does not find
+            them there; returns (ms, replicas)."""
+            q0, k0, v0 = dense_inputs(cfg)
+            per = (2 * q0.numel() * q0.element_size() + (k0.numel() + v0.numel()) * k0.element_size()
+                   + cfg.B * cfg.Hq * cfg.Lq * 4)  # q, k, v, out, lse
+            n_rep = max(1, min(64, math.ceil(KV_ROTATION_BYTES / per)))
+            reps = [tuple(t.to(dev) for t in (q0, k0, v0)) + (torch.empty(q0.shape, dtype=q0.dtype, device=dev),
+                    torch.empty((cfg.B, cfg.Hq, cfg.Lq), dtype=torch.float32, device=dev)) for _ in range(n_rep)]
+            n = max(iters, n_rep)
+
+            def launch(i):
+                qq, kk, vv, o, l = reps[i % n_rep]
                 ta.attn_fwd(qq, kk, vv, out=o, lse=l, scale=cfg.scale, causal=cfg.causal, window=cfg.window,
                             stream=stream)
+
+            for i in range(min(3, n_rep) if n_rep > 1 else 3):
+                launch(i)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(n):
+                launch(i)
             e1.record(stream)
             torch.cuda.synchronize()
-            return e0.elapsed_time(e1) / iters
+            del reps
+            return e0.elapsed_time(e1) / n, n_rep
 
         for name in ("gqa8k_window", "std2048", "std2048_causal", "std512", "std512_causal", "vit", "tiny"):
             cfg = CONFIGS[name]
-            ms = time_fwd(cfg)
+            ms, n_rep_f = time_fwd(cfg)
             if cfg.window >= 0:
                 fl = 4.0 * cfg.B * cfg.Hq * cfg.D * window_pairs(cfg.Lq, cfg.Lk, cfg.window, cfg.causal)
             else:
@@ -476,7 +515,7 @@ def main():
                 + cfg.B * cfg.Hq * cfg.Lq * 4
             detail[name] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(fl / ms / 1e9, 1),
                             "frac_mfma": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
-                            "GB/s": round(byts / ms / 1e6, 1)}
+                            "GB/s": round(byts / ms / 1e6, 1), "input_replicas": n_rep_f}
             # attainable roofline min(MFMA peak, AI x HBM peak)
             attain = min(PEAK_BF16_TFLOPS, fl / byts * PEAK_HBM_GBS / 1e3)
             detail[name]["frac_attainable"] = round(fl / ms / 1e9 / attain, 4)
@@ -520,7 +559,7 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / 10
-        ms_plain = time_fwd(dcfg)
+        ms_plain, _ = time_fwd(dcfg)
         fl = causal_flops(dcfg.B, dcfg.Hq, dcfg.Lq, dcfg.Lk, dcfg.D, True)
         detail["dropout_gqa8k_causal"] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(fl / ms / 1e9, 1),
                                           "frac_mfma": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4),

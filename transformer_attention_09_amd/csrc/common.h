@@ -78,6 +78,10 @@ struct F16 {
   static __device__ __forceinline__ float to_f32(elem x) { return (float)x; }
 };
 
+// Cache-policy operand of the buffer intrinsics on gfx950: bit 1 is NT
+// (non-temporal: streamed data that should not stay in the caches).
+constexpr int kCachePolicyNT = 2;
+
 // Raw buffer access: a 128-bit resource (base, byte range) lets a load outside
 // [0, bytes) return zeros without a branch.  The third word is the gfx9-family
 // default (raw, untyped, 32-bit data).
