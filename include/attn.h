@@ -108,14 +108,17 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
  *   out[b,i,h,:] = sum_j P[i,j] * keep(b,h,i,j) * v[b,j,g,:] / (1 - dropout_p)
  *
  * with P the row softmax of attn_fwd; lse is attn_fwd's (the undropped row
- * statistic), which attn_bwd_dropout needs.  keep(b,h,i,j) is 1 iff word j%4
- * of Philox4x32-10 (Salmon, Moraes, Dror, Shaw: "Parallel Random Numbers:
- * As Easy as 1, 2, 3", SC 2011) at the counter (j/4, i, b*Hq + h, offset)
- * under the key (seed mod 2^32, seed / 2^32) is >= floor(dropout_p * 2^32),
- * so each probability is kept with probability 1 - dropout_p (exactly, for
- * dropout_p a multiple of 2^-32), independently of the others, and any
- * element's decision can be recomputed on its own (the backward does).
- * 1 / (1 - dropout_p) is applied in fp32 with the output normalisation.
+ * statistic), which attn_bwd_dropout needs.  keep(b,h,i,j) is 1 iff the
+ * 16-bit half (low for even i, high for odd i) of word j%4 of Philox4x32-10
+ * (Salmon, Moraes, Dror, Shaw: "Parallel Random Numbers: As Easy as 1, 2, 3",
+ * SC 2011) at the counter (j/4, i/2, b*Hq + h, offset) under the key
+ * (seed mod 2^32, seed / 2^32) is >= floor(dropout_p * 2^16): one generator
+ * call decides four keys of two neighbouring rows.  Each probability is kept
+ * with probability 1 - floor(dropout_p * 2^16) / 2^16 (1 - dropout_p exactly
+ * for dropout_p a multiple of 2^-16, and never more than 2^-16 above it),
+ * independently of the others, and any element's decision can be recomputed
+ * on its own (the backward does).  1 / (1 - dropout_p) is applied in fp32
+ * with the output normalisation.
  */
 int attn_fwd_dropout(const void* q, const void* k, const void* v, void* out, float* lse,
                      int B, int Hq, int Hkv, int Lq, int Lk, int D,

@@ -15,10 +15,15 @@ more.  The readings taken here:
     1, 2, 3" (SC 2011), so that any element's decision can be computed on its
     own, in any order, on either side;
   * element (b, h, i, j) (batch, query head, query row, key) takes word
-    j mod 4 of Philox4x32-10 at counter (floor(j / 4), i, b * Hq + h, offset)
-    under the key (seed mod 2^32, floor(seed / 2^32)); it is kept iff that
-    32-bit word is >= floor(p * 2^32), with p the float32 value of dropout_p
-    and 0 <= p < 1.
+    j mod 4 of Philox4x32-10 at counter (floor(j / 4), floor(i / 2),
+    b * Hq + h, offset) under the key (seed mod 2^32, floor(seed / 2^32)),
+    and of that word the low 16 bits for even i, the high 16 bits for odd i;
+    it is kept iff that 16-bit number is >= floor(p * 2^16), with p the
+    float32 value of dropout_p and 0 <= p < 1.  One generator call thus
+    decides four keys of two neighbouring rows.  The keep probability is
+    1 - floor(p * 2^16) / 2^16, which is 1 - p for p a multiple of 2^-16 and
+    otherwise above 1 - p by less than 2^-16; the kept values are still
+    scaled by 1 / (1 - p).
 """
 from __future__ import annotations
 
@@ -64,11 +69,11 @@ def philox4x32(counter, key, rounds: int = PHILOX_ROUNDS) -> np.ndarray:
 
 
 def dropout_threshold(p: float) -> int:
-    """The 32-bit threshold of dropout probability p (as float32): floor(p * 2^32)."""
+    """The 16-bit threshold of dropout probability p (as float32): floor(p * 2^16)."""
     p32 = float(np.float32(p))
     if not (0.0 <= p32 < 1.0):
         raise ValueError(f"dropout probability must lie in [0, 1), got {p}")
-    return int(math.floor(p32 * 2.0 ** 32))
+    return int(math.floor(p32 * 2.0 ** 16))
 
 
 def dropout_keep(bh: int, rows, Lk: int, p: float, seed: int, offset: int, key0: int = 0) -> np.ndarray:
@@ -79,13 +84,14 @@ def dropout_keep(bh: int, rows, Lk: int, p: float, seed: int, offset: int, key0:
     g0, g1 = key0 // 4, (key0 + Lk + 3) // 4  # the 4-key groups that cover the keys
     ctr = np.empty((len(i), g1 - g0, 4), dtype=np.uint64)
     ctr[..., 0] = np.arange(g0, g1, dtype=np.uint64)[None, :]
-    ctr[..., 1] = i.astype(np.uint64)[:, None]
+    ctr[..., 1] = (i // 2).astype(np.uint64)[:, None]
     ctr[..., 2] = np.uint64(bh)
     ctr[..., 3] = np.uint64(offset & 0xFFFFFFFF)
     words = philox4x32(ctr, (seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF))
     first = key0 - 4 * g0
-    words = words.reshape(len(i), 4 * (g1 - g0))[:, first:first + Lk]
-    return words.astype(np.uint64) >= np.uint64(thr)
+    words = words.reshape(len(i), 4 * (g1 - g0))[:, first:first + Lk].astype(np.uint64)
+    halves = (words >> (np.uint64(16) * (i % 2).astype(np.uint64))[:, None]) & np.uint64(0xFFFF)
+    return halves >= np.uint64(thr)
 
 
 def attention_dropout(q, k, v, scale: float, causal: bool = False, window: int = -1,

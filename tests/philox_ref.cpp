@@ -5,8 +5,9 @@
 //   philox_ref words   reads "k0 k1 c0 c1 c2 c3" lines (c1 < 2^30), prints the
 //                      four output words of counter (c0,c1,c2,c3) under key (k0,k1)
 //   philox_ref keep    reads "seed offset thr bh i j" lines, prints 1 if element
-//                      (bh, i, j) is kept: word j%4 of counter (j/4, i, bh, offset)
-//                      under key (seed low, seed high) is >= thr
+//                      (bh, i, j) is kept: of word j%4 of counter (j/4, i/2, bh,
+//                      offset) under key (seed low, seed high), the low 16 bits
+//                      for even i and the high 16 bits for odd i, are >= thr
 //
 // The engine's state is (key = seed, counter = (offset/4 as 64 bits,
 // subsequence as 64 bits)), and next() returns word offset%4 of it.
@@ -30,9 +31,10 @@ int main(int argc, char** argv) {
   if (!strcmp(argv[1], "keep")) {
     unsigned long long seed, off, thr, bh, i, j;
     while (scanf("%llu %llu %llu %llu %llu %llu", &seed, &off, &thr, &bh, &i, &j) == 6) {
-      if (i >= (1ull << 30)) return 3;
-      rocrand_device::philox4x32_10_engine e(seed, bh | (off << 32), 4ull * ((j / 4) | (i << 32)) + j % 4);
-      printf("%d\n", (unsigned long long)e.next() >= thr ? 1 : 0);
+      if (i / 2 >= (1ull << 30)) return 3;
+      rocrand_device::philox4x32_10_engine e(seed, bh | (off << 32), 4ull * ((j / 4) | ((i / 2) << 32)) + j % 4);
+      const unsigned long long half = ((unsigned long long)e.next() >> (16 * (i % 2))) & 0xFFFFull;
+      printf("%d\n", half >= thr ? 1 : 0);
     }
     return 0;
   }

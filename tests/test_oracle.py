@@ -633,10 +633,11 @@ def test_p14_philox_matches_library_engine(philox_ref):
 
 def test_p14_keep_convention_matches_library_engine(philox_ref):
     # element (bh, i, j) against the engine addressed per element, over rows and
-    # keys that cross 4-key groups, large row and key indexes, offsets and seeds
-    for (seed, off, p, bh, rows, Lk) in [(0, 0, 0.1, 0, [0, 1, 5], 13),
-                                          (0x1234567890ABCDEF, 77, 0.5, 37, [0, 9, 1000, 65535], 70),
-                                          (2 ** 64 - 1, 2 ** 32 - 1, 0.9, 2 ** 20 + 3, [3, 2 ** 29], 9)]:
+    # keys that cross 4-key groups and row pairs, both rows of a pair, large
+    # row and key indexes, offsets and seeds
+    for (seed, off, p, bh, rows, Lk) in [(0, 0, 0.1, 0, [0, 1, 2, 3, 5], 13),
+                                          (0x1234567890ABCDEF, 77, 0.5, 37, [0, 9, 8, 1000, 1001, 65535], 70),
+                                          (2 ** 64 - 1, 2 ** 32 - 1, 0.9, 2 ** 20 + 3, [3, 2 ** 29, 2 ** 31 - 1], 9)]:
         thr = oracle.dropout_threshold(p)
         keep = oracle.dropout_keep(bh, rows, Lk, p, seed, off)
         qs = [(seed, off, thr, bh, i, j) for i in rows for j in range(Lk)]
@@ -651,7 +652,7 @@ def test_p14_keep_with_key_offset(philox_ref):
     for key0 in (1, 4, 37, 101):
         part = oracle.dropout_keep(3, [0, 7, 40], 150 - key0, 0.3, 99, 4, key0=key0)
         assert np.array_equal(part, full[:, key0:])
-    key0, n, rows = (1 << 30) + 3, 21, [5, 2 ** 20]
+    key0, n, rows = (1 << 30) + 3, 21, [5, 2 ** 20, 2 ** 20 + 1]
     thr = oracle.dropout_threshold(0.4)
     keep = oracle.dropout_keep(11, rows, n, 0.4, 77, 9, key0=key0)
     want = philox_ref("keep", [(77, 9, thr, 11, i, key0 + c) for i in rows for c in range(n)])
@@ -660,10 +661,11 @@ def test_p14_keep_with_key_offset(philox_ref):
 
 def test_p14_threshold_and_validation():
     assert oracle.dropout_threshold(0.0) == 0
-    assert oracle.dropout_threshold(0.5) == 2 ** 31
-    assert oracle.dropout_threshold(0.25) == 2 ** 30
+    assert oracle.dropout_threshold(0.5) == 2 ** 15
+    assert oracle.dropout_threshold(0.25) == 2 ** 14
+    assert oracle.dropout_threshold(np.nextafter(np.float32(1), np.float32(0))) == 2 ** 16 - 1
     p32 = float(np.float32(0.1))
-    assert oracle.dropout_threshold(0.1) == math.floor(p32 * 2 ** 32)
+    assert oracle.dropout_threshold(0.1) == math.floor(p32 * 2 ** 16) == 6553
     for bad in (1.0, -0.01, 1.5, float("nan")):
         with pytest.raises(ValueError):
             oracle.dropout_threshold(bad)
@@ -673,7 +675,8 @@ def test_p14_threshold_and_validation():
 def test_p14_keep_rate_is_one_minus_p(p):
     # 2 heads x 300 rows x 700 keys = 420,000 independent decisions: the kept
     # fraction must lie within 5 binomial standard deviations of 1 - p, in
-    # total and for each of the four words of a Philox output
+    # total, for each of the four words of a Philox output and for each of its
+    # two 16-bit halves (even and odd rows)
     keep = np.concatenate([oracle.dropout_keep(bh, np.arange(300), 700, p, 99, 3) for bh in (0, 1)])
     n = keep.size
     sd = math.sqrt(p * (1 - p) / n)
@@ -681,6 +684,13 @@ def test_p14_keep_rate_is_one_minus_p(p):
     for w in range(4):
         kw = keep[:, w::4]
         assert abs(kw.mean() - (1 - p)) < 5 * math.sqrt(p * (1 - p) / kw.size)
+    for half in range(2):
+        kh = keep[half::2]
+        assert abs(kh.mean() - (1 - p)) < 5 * math.sqrt(p * (1 - p) / kh.size)
+    # the two rows of a pair share each generator call but not its bits
+    x = keep.astype(float) - keep.mean()
+    pair = (x[0::2] * x[1::2]).mean() / x.var()
+    assert abs(pair) < 5 / math.sqrt(x[0::2].size)
     # neighbouring decisions are uncorrelated (lag-1 along keys and rows)
     x = keep.astype(float) - keep.mean()
     for a, b in ((x[:, 1:], x[:, :-1]), (x[1:], x[:-1])):

@@ -210,17 +210,37 @@ def _keep_inverted(bh, rows, Lk, p, seed, offset, key0=0):
     return ~_orig_keep(bh, rows, Lk, p, seed, offset, key0)
 
 
-def _keep_row_key_swapped(bh, rows, Lk, p, seed, offset, key0=0):
+def _keep_halves(rows, words, flip=False):
+    par = (np.asarray(rows) % 2).astype(np.uint64)
+    if flip:
+        par = np.uint64(1) - par
+    return (words.astype(np.uint64) >> (np.uint64(16) * par)[:, None]) & np.uint64(0xFFFF)
+
+
+def _keep_variant(bh, rows, Lk, p, seed, offset, key0=0, swap_row_key=False, flip_halves=False, full_row=False):
     rows = np.asarray(rows)
     thr = OD.dropout_threshold(p)
     g0, g1 = key0 // 4, (key0 + Lk + 3) // 4
     ctr = np.zeros((len(rows), g1 - g0, 4), dtype=np.uint64)
-    ctr[..., 0] = rows[:, None]
-    ctr[..., 1] = np.arange(g0, g1)[None, :]
+    rpair = rows if full_row else rows // 2
+    ctr[..., 0] = rpair[:, None] if swap_row_key else np.arange(g0, g1)[None, :]
+    ctr[..., 1] = np.arange(g0, g1)[None, :] if swap_row_key else rpair[:, None]
     ctr[..., 2] = bh
     ctr[..., 3] = offset
     w = OD.philox4x32(ctr, (seed & 0xFFFFFFFF, seed >> 32)).reshape(len(rows), 4 * (g1 - g0))
-    return w[:, key0 - 4 * g0:key0 - 4 * g0 + Lk] >= thr
+    return _keep_halves(rows, w[:, key0 - 4 * g0:key0 - 4 * g0 + Lk], flip_halves) >= thr
+
+
+def _keep_row_key_swapped(bh, rows, Lk, p, seed, offset, key0=0):
+    return _keep_variant(bh, rows, Lk, p, seed, offset, key0, swap_row_key=True)
+
+
+def _keep_halves_swapped(bh, rows, Lk, p, seed, offset, key0=0):
+    return _keep_variant(bh, rows, Lk, p, seed, offset, key0, flip_halves=True)
+
+
+def _keep_row_not_paired(bh, rows, Lk, p, seed, offset, key0=0):
+    return _keep_variant(bh, rows, Lk, p, seed, offset, key0, full_row=True)
 
 
 def _keep_word_order_reversed(bh, rows, Lk, p, seed, offset, key0=0):
@@ -306,6 +326,8 @@ MUTANTS = {
     "philox_hi_lo_swapped": ("philox4x32", _philox_variant(swap_hi_lo=True)),
     "keep_inverted": ("dropout_keep", _keep_inverted),
     "keep_row_key_swapped": ("dropout_keep", _keep_row_key_swapped),
+    "keep_halves_swapped": ("dropout_keep", _keep_halves_swapped),
+    "keep_row_not_paired": ("dropout_keep", _keep_row_not_paired),
     "keep_word_order_reversed": ("dropout_keep", _keep_word_order_reversed),
     "dropout_renormalised": ("attention_dropout", _attn_drop_variant("renormalised")),
     "dropout_unscaled": ("attention_dropout", _attn_drop_variant("unscaled")),

@@ -117,8 +117,8 @@ int fwd_dense(const void* q, const void* k, const void* v, void* out, float* lse
   a.ctx_lens = nullptr;
   a.max_blocks_per_seq = 0;
   a.num_blocks = 0;
-  // threshold floor(p * 2^32): exact in double, below 2^32 for p < 1
-  a.drop_thr = drop ? (uint32_t)std::floor((double)dropout_p * 4294967296.0) : 0u;
+  // threshold floor(p * 2^16): exact in double, below 2^16 for p < 1
+  a.drop_thr = drop ? (uint32_t)std::floor((double)dropout_p * 65536.0) : 0u;
   a.drop_scale = drop ? (float)(1.0 / (1.0 - (double)dropout_p)) : 1.f;
   a.seed_lo = (uint32_t)seed;
   a.seed_hi = (uint32_t)(seed >> 32);
@@ -278,7 +278,7 @@ int bwd_common(const void* q, const void* k, const void* v, const void* out, con
   a.scale_log2 = scale * attn::kLog2e;
   a.n_qblocks = (int)n_qblocks;
   // the forward's threshold and scale (attn_fwd_dropout)
-  a.drop_thr = drop ? (uint32_t)std::floor((double)dropout_p * 4294967296.0) : 0u;
+  a.drop_thr = drop ? (uint32_t)std::floor((double)dropout_p * 65536.0) : 0u;
   a.drop_scale = drop ? (float)(1.0 / (1.0 - (double)dropout_p)) : 1.f;
   a.seed_lo = (uint32_t)seed;
   a.seed_hi = (uint32_t)(seed >> 32);

@@ -33,11 +33,13 @@
 // M = keep / (1 - p); then dV = (P * M)^T dO and dS = P * (M * dP - D), where
 // D_i = sum_d dO_id O_id still equals sum_j P_ij M_ij dP_ij.  Both kernels
 // recompute the keep decisions with the forward's Philox counter
-// (j/4, i, b*Hq + h, offset): one call gives a row's four keys 4c..4c+3.  The
-// dQ kernel holds a row per lane and four consecutive keys per register
-// group, as the forward does; the dK/dV kernel holds a key per lane, so the
-// four lanes of a quad (four consecutive keys) each draw one row's call and
-// trade words with a 4x4 quad transpose.
+// (j/4, i/2, b*Hq + h, offset): one call gives the four keys 4c..4c+3 of the
+// rows 2m (low 16 bits of each word) and 2m+1 (high 16 bits).  The dQ kernel
+// holds a row per lane and four consecutive keys per register group, as the
+// forward does, and the two lanes of a row pair split the calls; the dK/dV
+// kernel holds a key per lane, so the four lanes of a quad (four consecutive
+// keys) each draw two row pairs' calls and trade words with a 4x4 quad
+// transpose.
 #include <hip/hip_runtime.h>
 
 #include "common.h"
@@ -246,23 +248,33 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
     {
       const int rb = rh;
       // Dropout: bit r of kbits keeps the element of accumulator register r
-      // (row 8*(r/4) + 4*hh + r%4 of the block, this lane's key).  Lane q of a
-      // quad draws the call of row 8*(r/4) + 4*hh + q for the quad's four
-      // keys; the transpose hands each lane its key's word of the four rows.
-      // Drawn before the products, while few registers are live.
+      // (row 8*(r/4) + 4*hh + r%4 of the block, this lane's key).  A call
+      // decides the quad's four keys for a pair of rows (registers 2m, 2m+1):
+      // lane q of a quad draws the pairs of registers 8s + 2q (s = 0, 1), and
+      // the transpose hands each lane its key's word of the four lanes' calls,
+      // so the word of lane c in round s holds registers 8s + 2c (low half)
+      // and 8s + 2c + 1 (high half).  Drawn before the products, while few
+      // registers are live.
       uint32_t kbits = 0u;
       if constexpr (DROP) {
+        const uint32_t thr2 = a.drop_thr | (a.drop_thr << 16);
+        uint32_t drop = 0u;
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          uint32_t row = (uint32_t)(i0 + rb * 32 + 8 * r4 + 4 * hh + (l32 & 3));
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const int q = l32 & 3;
+          uint32_t row = (uint32_t)(i0 + rb * 32 + 4 * hh + 8 * ((q >> 1) + 2 * s2) + 2 * (q & 1));
           uint32_t c0 = (uint32_t)(key >> 2), k0 = a.seed_lo, k1 = a.seed_hi;
           asm volatile("" : "+v"(row), "+v"(c0), "+s"(k0), "+s"(k1));
-          const uint4 r = philox4x32_10(make_uint4(c0, row, drop_bh, a.drop_offset), k0, k1);
+          const uint4 r = philox4x32_10(make_uint4(c0, row >> 1, drop_bh, a.drop_offset), k0, k1);
           uint32_t w[4] = {r.x, r.y, r.z, r.w};
-          quad_transpose(w, l32 & 3);
+          quad_transpose(w, q);
 #pragma unroll
-          for (int c = 0; c < 4; ++c) kbits |= (w[c] >= a.drop_thr ? 1u : 0u) << (4 * r4 + c);
+          for (int c = 0; c < 4; ++c) {
+            const uint32_t f = drop_flags2(w[c], thr2, 0x00010001u);
+            drop |= ((f & 1u) | ((f >> 15) & 2u)) << (8 * s2 + 2 * c);
+          }
         }
+        kbits = ~drop & 0xFFFFu;
       }
       f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
@@ -534,18 +546,13 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256, SPLIT ? 1 : 2) void bwd_dq_kerne
                       (wr_lo + 31 < a.Lq);
     uint32_t pw[4][4];
     // Dropout: bit 16*kh + r keeps register r of half kh; registers 4g'..4g'+3
-    // of half kh are the words of the call with counter word 0 = 16*t + 2*(4*kh + g') + hh.
+    // of half kh are the keys of the 4-key group with counter word 0 =
+    // 16*t + 2*(4*kh + g') + hh, and the two rows of a pair sit in lanes l, l^1.
     uint32_t kbits = 0u;
     if constexpr (DROP) {
       uint32_t c0 = (uint32_t)(16 * t + hh), row = (uint32_t)qi, k0 = a.seed_lo, k1 = a.seed_hi;
       asm volatile("" : "+v"(c0), "+v"(row), "+s"(k0), "+s"(k1));
-#pragma unroll
-      for (int g4 = 0; g4 < 8; ++g4) {
-        const uint4 r = philox4x32_10(make_uint4(c0 + 2 * g4, row, drop_bh, a.drop_offset), k0, k1);
-        const uint32_t th = a.drop_thr;
-        kbits |= ((r.x >= th ? 1u : 0u) | (r.y >= th ? 2u : 0u) | (r.z >= th ? 4u : 0u) | (r.w >= th ? 8u : 0u))
-                 << (4 * g4);
-      }
+      kbits = keep_bits_row_pair(c0, row, drop_bh, a.drop_offset, k0, k1, a.drop_thr);
     }
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {

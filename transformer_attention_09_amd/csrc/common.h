@@ -304,12 +304,17 @@ constexpr float kLn2 = 0.69314718055994530942f;
 // hi(w0-product) ^ x3 ^ k1, lo(w0-product)); the key grows by the Weyl
 // increments (0x9E3779B9, 0xBB67AE85) after every round.  The key is
 // wave-uniform where it is used, so its schedule runs on the scalar unit.
+// A round is two v_mad_u64_u32 and two three-input XORs (v_bitop3_b32 with
+// the truth table of a ^ b ^ c).
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
 __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
     const uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
     const uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
-    c = make_uint4((uint32_t)(p1 >> 32) ^ c.y ^ k0, (uint32_t)p1, (uint32_t)(p0 >> 32) ^ c.w ^ k1, (uint32_t)p0);
+    c = make_uint4(xor3((uint32_t)(p1 >> 32), c.y, k0), (uint32_t)p1, xor3((uint32_t)(p0 >> 32), c.w, k1), (uint32_t)p0);
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
   }
@@ -335,6 +340,64 @@ __device__ __forceinline__ void quad_transpose(uint32_t (&x)[4], int q) {
     const uint32_t r = (uint32_t)__builtin_amdgcn_mov_dpp((int)(hi ? x[e] : x[e + 2]), kSwap2, 0xF, 0xF, false);
     if (hi) x[e] = r; else x[e + 2] = r;
   }
+}
+
+// Dropout keep decisions.  Element (row i, key j) of head bh takes word j % 4
+// of Philox4x32-10 at counter (j / 4, i / 2, bh, offset) under the seed's key;
+// of that word the low 16 bits for even i and the high 16 bits for odd i; it
+// is kept iff that number is >= thr = floor(p * 2^16).  One call thus decides
+// four keys of two neighbouring rows.
+//
+// Drop flags of both halves of a word w: bit 0 set iff its low 16 bits are
+// below thr, bit 16 iff its high 16 bits are (thr2 holds thr in both halves,
+// ones2 holds 1 in both).  The saturating packed difference thr - half is
+// zero exactly when the half is kept, and its minimum with 1 is the flag.
+// (Written out: the compiler turns the same packed builtins into a compare,
+// a select and a permute per half.)
+__device__ __forceinline__ uint32_t drop_flags2(uint32_t w, uint32_t thr2, uint32_t ones2) {
+  uint32_t d;
+  asm("v_pk_sub_u16 %0, %1, %2 clamp\n\t"
+      "v_pk_min_u16 %0, %0, %3"
+      : "=&v"(d)
+      : "s"(thr2), "v"(w), "s"(ones2));
+  return d;
+}
+
+// Nibble k of a 16-bit value moved to bits 8k .. 8k+3.
+__device__ __forceinline__ uint32_t spread_nibbles(uint32_t x) {
+  x = ((x << 8) | x) & 0x00FF00FFu;
+  return ((x << 4) | x) & 0x0F0F0F0Fu;
+}
+
+// Keep bits of one row over eight 4-key groups whose counter words 0 are
+// c0 + 2g (g = 0..7): bit 4g + (key % 4), set = kept.  For layouts with one
+// row per lane in which the other row of the pair (row ^ 1) is in lane ^ 1
+// (and every lane of the wave is active): each lane draws the four calls of
+// the groups g with g % 2 == row % 2 and the two lanes trade the decisions
+// for each other's row.
+__device__ __forceinline__ uint32_t keep_bits_row_pair(uint32_t c0, uint32_t row, uint32_t bh, uint32_t offset,
+                                                       uint32_t k0, uint32_t k1, uint32_t thr) {
+  const uint32_t par = row & 1u;
+  const uint32_t thr2 = thr | (thr << 16), ones2 = 0x00010001u;
+  uint32_t acc = 0u;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint4 r = philox4x32_10(make_uint4(c0 + 2u * par + 4u * (uint32_t)k, row >> 1, bh, offset), k0, k1);
+    acc = (acc << 1) | drop_flags2(r.x, thr2, ones2);
+    acc = (acc << 1) | drop_flags2(r.y, thr2, ones2);
+    acc = (acc << 1) | drop_flags2(r.z, thr2, ones2);
+    acc = (acc << 1) | drop_flags2(r.w, thr2, ones2);
+  }
+  // Word n = 4k + w has its low-half flag at bit 15 - n and its high-half
+  // flag at bit 31 - n; reversed, the high-half flags sit at bits n and the
+  // low-half flags at bits 16 + n.
+  const uint32_t rev = __builtin_bitreverse32(acc);
+  const uint32_t lo = rev >> 16, hi = rev & 0xFFFFu;
+  const uint32_t mine = spread_nibbles(par ? hi : lo) << (4u * par);
+  const uint32_t other = spread_nibbles(par ? lo : hi) << (4u * par);
+  constexpr int kSwapPairs = 1 | (0 << 2) | (3 << 4) | (2 << 6);  // quad_perm [1,0,3,2]
+  const uint32_t got = (uint32_t)__builtin_amdgcn_mov_dpp((int)other, kSwapPairs, 0xF, 0xF, false);
+  return ~(mine | got);
 }
 
 // f(std::integral_constant<int, i>) for i = 0..N-1, expanded at compile time,

@@ -227,7 +227,9 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256, SPLIT ? 1 : 2) void fwd_kernel(F
   uint32_t qsign = 0u, qkeep = 0xffffffffu;
   if (sl2 < 0.f) { qsign = 0x80008000u; sl2 = -sl2; }
   if (sl2 == 0.f) { qkeep = 0u; sl2 = 1.f; }
-  V8 qf[C::KSTEPS];
+  // The loads are issued here and their values used only after the first
+  // K/V tiles have been requested, so the two memory round trips overlap.
+  uint4 qw[C::KSTEPS];
   {
     // Rows q0.. of this head: row i at (i - q0) * Hq * D elements; rows past
     // Lq read as zeros through the resource range.
@@ -235,13 +237,18 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256, SPLIT ? 1 : 2) void fwd_kernel(F
     const rsrc_t qr = make_rsrc(qbase, rows_range(a.Lq - q0, (size_t)a.Hq * D, D, sizeof(E)));
     const uint32_t qo = (uint32_t)(((size_t)(wave * 32 + l32) * a.Hq * D + 8 * hh) * sizeof(E));
 #pragma unroll
+    for (int s = 0; s < C::KSTEPS; ++s) qw[s] = buf_load16(qr, qo + 32 * s);
+  }
+  V8 qf[C::KSTEPS];
+  auto finish_q = [&]() {
+#pragma unroll
     for (int s = 0; s < C::KSTEPS; ++s) {
-      uint4 w = buf_load16(qr, qo + 32 * s);
+      uint4 w = qw[s];
       w.x = (w.x ^ qsign) & qkeep; w.y = (w.y ^ qsign) & qkeep;
       w.z = (w.z ^ qsign) & qkeep; w.w = (w.w ^ qsign) & qkeep;
       qf[s] = __builtin_bit_cast(V8, w);
     }
-  }
+  };
   // Keys this row may see: [jlo_row, jhi_row] (empty when jhi_row < jlo_row).
   int jlo_row = 0, jhi_row = Lk - 1;
   if (a.causal) jhi_row = min(jhi_row, qi + off);
@@ -373,24 +380,17 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256, SPLIT ? 1 : 2) void fwd_kernel(F
 
   // Dropout decisions of a tile's 32 elements in this lane, bit e for
   // element e.  Element e is key 8*(e/4) + 4*hh + e%4 of the tile, so the
-  // elements 4g..4g+3 are the four words of one Philox call whose counter
-  // word 0 is 16*t + 2*g + hh.
+  // elements 4g..4g+3 are the four words of the call whose counter word 0 is
+  // 16*t + 2*g + hh; the two rows of a pair sit in lanes l and l^1.
   // The empty asm statement makes the counter and the key opaque at each
   // call, so the compiler can neither hoist the parts of the rounds that do
   // not depend on the tile out of the key loop nor turn the products of
   // word 0 into induction variables: either would keep values live across
   // the loop, which has no registers to spare.
   auto draw_tile = [&](int t) -> uint32_t {
-    uint32_t bits = 0u;
-    const uint32_t th = a.drop_thr;
     uint32_t c0 = (uint32_t)(16 * t + hh), row = (uint32_t)qi, bh = drop_bh, k0 = a.seed_lo, k1 = a.seed_hi;
     asm volatile("" : "+v"(c0), "+v"(row), "+s"(bh), "+s"(k0), "+s"(k1));
-#pragma unroll
-    for (int g4 = 0; g4 < 8; ++g4) {
-      const uint4 r = philox4x32_10(make_uint4(c0 + 2 * g4, row, bh, a.drop_offset), k0, k1);
-      bits |= ((r.x >= th ? 1u : 0u) | (r.y >= th ? 2u : 0u) | (r.z >= th ? 4u : 0u) | (r.w >= th ? 8u : 0u)) << (4 * g4);
-    }
-    return bits;
+    return keep_bits_row_pair(c0, row, bh, a.drop_offset, k0, k1, a.drop_thr);
   };
   uint32_t kbits = 0u;  // decisions of the current tile (dropout only)
 
@@ -584,6 +584,8 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256, SPLIT ? 1 : 2) void fwd_kernel(F
       load_v(t_lo + hf, vt0, 0);
       load_k(t_lo + hf + TS, kt1, 0);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    finish_q();
     wait_vmem();
     __syncthreads();
     scur[0] = f32x16{};

@@ -26,9 +26,10 @@ struct FwdArgs {
   const int32_t* ctx_lens;
   int max_blocks_per_seq, num_blocks;
   // Dropout on the probabilities (attn_fwd_dropout): element (b, h, i, j) is
-  // kept iff word j%4 of Philox4x32-10 at counter (j/4, i, b*Hq+h,
-  // drop_offset) under key (seed_lo, seed_hi) is >= drop_thr; kept ones
-  // are scaled by drop_scale = 1/(1-p).  Unused by the other entry points.
+  // kept iff the 16-bit half (low for even i, high for odd i) of word j%4 of
+  // Philox4x32-10 at counter (j/4, i/2, b*Hq+h, drop_offset) under key
+  // (seed_lo, seed_hi) is >= drop_thr (= floor(p * 2^16)); kept ones are
+  // scaled by drop_scale = 1/(1-p).  Unused by the other entry points.
   uint32_t drop_thr, seed_lo, seed_hi, drop_offset;
   float drop_scale;
   // Split each work-group's key tiles between two 4-wave halves (set when
