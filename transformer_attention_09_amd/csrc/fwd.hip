@@ -489,8 +489,18 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256, SPLIT ? 1 : 2) void fwd_kernel(F
       // keep the sum here, between the MFMAs, instead of letting it sink
       // below the loop's barrier where nothing overlaps it
       asm volatile("" : "+v"(rs));
-      if constexpr (DROP) px[e] = (kbits >> e) & 1u ? px[e] : 0.f;  // the row sum keeps every probability
-      if (e & 1) pw[e >> 3][(e & 7) >> 1] = pack2<TT>(px[e - 1], px[e]);
+      if (e & 1) {
+        uint32_t w = pack2<TT>(px[e - 1], px[e]);
+        // Dropped probabilities are zeroed in the packed operand only (the
+        // row sum keeps every probability): each keep bit, sign-extended,
+        // masks its 16-bit half.
+        if constexpr (DROP) {
+          const uint32_t lo = (uint32_t)__builtin_amdgcn_sbfe((int)kbits, e - 1, 1);
+          const uint32_t hi = (uint32_t)__builtin_amdgcn_sbfe((int)kbits, e, 1);
+          w &= (lo & 0x0000FFFFu) | (hi & 0xFFFF0000u);
+        }
+        pw[e >> 3][(e & 7) >> 1] = w;
+      }
     };
     __builtin_amdgcn_sched_barrier(0);
     static_for<NSLOT + 2>([&](auto ic) {
