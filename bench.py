@@ -21,7 +21,9 @@ also compared with a plain streaming read on the same device
 (attn_hbm_read_probe, the attainable HBM rate) of its own size, rotated over
 2 GiB, and of 2 GiB; the shader clock is sampled with rocm-smi while a batch of
 forward launches runs.  The per-workload detail times each forward over input
-replicas totalling at least 1 GiB (up to 64), one per launch in turn.
+replicas totalling at least 1 GiB (up to 64), one per launch in turn, calling
+the C ABI with arguments marshalled once per replica; every detail timing
+follows half a second of untimed launches of the same workload.
 
     python bench.py [--gpus 1] [--steps K=100] [--warmup W=10] [--no-cpu] [--no-detail]
 
@@ -47,6 +49,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, published
 KV_ROTATION_BYTES = 1 << 30
 SETTLE_S = 1.0              # untimed steps before the warmup: the shader clock settles under sustained load
+DETAIL_SETTLE_S = 0.5       # untimed launches before each per-workload detail timing
 
 
 def log(*a):
@@ -485,6 +488,27 @@ def main():
     if not args.no_detail:
         detail = {}
 
+        def settled_ms(launch, n):
+            """Average time of n launches between two events on the launch
+            stream, after untimed launches for DETAIL_SETTLE_S seconds: each
+            detail workload's inputs are generated on the host first, and the
+            shader clock drops while the device waits for them."""
+            t_s, k = time.perf_counter(), 0
+            while True:
+                launch(k)
+                k += 1
+                if k % 4 == 0:
+                    torch.cuda.synchronize()
+                    if time.perf_counter() - t_s >= DETAIL_SETTLE_S:
+                        break
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(n):
+                launch(k + i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / n
+
         def time_fwd(cfg, iters=10):
             """Average launch time over input replicas totalling >= 1 GiB (at
             most 64 replicas), one replica per launch in turn, so that a
@@ -497,22 +521,20 @@ def main():
             reps = [tuple(t.to(dev) for t in (q0, k0, v0)) + (torch.empty(q0.shape, dtype=q0.dtype, device=dev),
                     torch.empty((cfg.B, cfg.Hq, cfg.Lq), dtype=torch.float32, device=dev)) for _ in range(n_rep)]
             n = max(iters, n_rep)
-
-            def launch(i):
-                qq, kk, vv, o, l = reps[i % n_rep]
-                ta.attn_fwd(qq, kk, vv, out=o, lse=l, scale=cfg.scale, causal=cfg.causal, window=cfg.window,
-                            stream=stream)
-
-            for i in range(min(3, n_rep) if n_rep > 1 else 3):
-                launch(i)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for i in range(n):
-                launch(i)
-            e1.record(stream)
-            torch.cuda.synchronize()
+            # The launches go straight to the C ABI with arguments marshalled
+            # once per replica: the short kernels here take less time than the
+            # binding's per-call checks, which would otherwise set the pace.
+            code = ta.ATTN_BF16 if q0.dtype == torch.bfloat16 else ta.ATTN_F16
+            fargs = [(qq.data_ptr(), kk.data_ptr(), vv.data_ptr(), o.data_ptr(), l.data_ptr(), cfg.B, cfg.Hq,
+                      cfg.Hkv, cfg.Lq, cfg.Lk, cfg.D, float(cfg.scale), int(bool(cfg.causal)), int(cfg.window), code,
+                      stream.cuda_stream) for (qq, kk, vv, o, l) in reps]
+            for i in range(n_rep):
+                st_ = lib.attn_fwd(*fargs[i])
+                if st_ != 0:
+                    raise RuntimeError(f"attn_fwd ({cfg.name}): {ta.attn_status_string(st_)}")
+            ms_ = settled_ms(lambda i: lib.attn_fwd(*fargs[i % n_rep]), n)
             del reps
-            return e0.elapsed_time(e1) / n, n_rep
+            return ms_, n_rep
 
         for name in ("gqa8k_window", "std2048", "std2048_causal", "std512", "std512_causal", "vit", "tiny"):
             cfg = CONFIGS[name]
@@ -537,15 +559,8 @@ def main():
             fq, fk, fv = (t.to(dev) for t in dense_inputs(cfg))
             fo = torch.empty(fq.shape, dtype=torch.bfloat16, device=dev)
             fl_ = torch.empty((cfg.B, cfg.Hq, cfg.Lq), dtype=torch.float32, device=dev)
-            for _ in range(3):
-                ta.attn_fwd_fp8(fq, fk, fv, out=fo, lse=fl_, scale=cfg.scale, causal=cfg.causal, stream=stream)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(10):
-                ta.attn_fwd_fp8(fq, fk, fv, out=fo, lse=fl_, scale=cfg.scale, causal=cfg.causal, stream=stream)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1) / 10
+            ms = settled_ms(lambda i: ta.attn_fwd_fp8(fq, fk, fv, out=fo, lse=fl_, scale=cfg.scale,
+                                                      causal=cfg.causal, stream=stream), 10)
             fl = causal_flops(cfg.B, cfg.Hq, cfg.Lq, cfg.Lk, cfg.D, cfg.causal)
             detail[name] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(fl / ms / 1e9, 1),
                             "frac_fp8_mfma": round(fl / ms / 1e9 / PEAK_FP8_TFLOPS, 4)}
@@ -553,23 +568,16 @@ def main():
             del fq, fk, fv, fo, fl_
 
         # forward with dropout (p = 0.1, the skill page's scenario 2 value) on the
-        # long causal GQA workload, beside the plain forward of the same launch shape
+        # long causal GQA workload, beside the plain forward on the same inputs,
+        # each after its own settling launches
         dcfg = CONFIGS["gqa8k_causal"]
         dq_, dk_, dv_ = (t.to(dev) for t in dense_inputs(dcfg))
         do_ = torch.empty_like(dq_)
         dl_ = torch.empty((dcfg.B, dcfg.Hq, dcfg.Lq), dtype=torch.float32, device=dev)
-        for _ in range(3):
-            ta.attn_fwd_dropout(dq_, dk_, dv_, 0.1, 1234, 0, out=do_, lse=dl_, scale=dcfg.scale, causal=True,
-                                stream=stream)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for it in range(10):
-            ta.attn_fwd_dropout(dq_, dk_, dv_, 0.1, 1234, it, out=do_, lse=dl_, scale=dcfg.scale, causal=True,
-                                stream=stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / 10
-        ms_plain, _ = time_fwd(dcfg)
+        ms = settled_ms(lambda it: ta.attn_fwd_dropout(dq_, dk_, dv_, 0.1, 1234, it, out=do_, lse=dl_,
+                                                       scale=dcfg.scale, causal=True, stream=stream), 10)
+        ms_plain = settled_ms(lambda it: ta.attn_fwd(dq_, dk_, dv_, out=do_, lse=dl_, scale=dcfg.scale, causal=True,
+                                                     stream=stream), 10)
         fl = causal_flops(dcfg.B, dcfg.Hq, dcfg.Lq, dcfg.Lk, dcfg.D, True)
         detail["dropout_gqa8k_causal"] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(fl / ms / 1e9, 1),
                                           "frac_mfma": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
@@ -593,15 +601,7 @@ def main():
                 ta.attn_bwd(bq, bk, bv, bo, bdo, bl, dq=bdq, dk=bdk, dv=bdv, scale=cfg.scale, causal=cfg.causal,
                             window=cfg.window, workspace=bws, stream=stream)
 
-            for _ in range(2):
-                backward()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(5):
-                backward()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1) / 5
+            ms = settled_ms(lambda i: backward(), 5)
             fl = 2.5 * causal_flops(cfg.B, cfg.Hq, cfg.Lq, cfg.Lk, cfg.D, cfg.causal)
             detail["bwd_" + name] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(fl / ms / 1e9, 1),
                                      "frac_mfma": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
@@ -615,14 +615,7 @@ def main():
                     ta.attn_bwd_dropout(bq, bk, bv, bo, bdo, bl, 0.1, 1234, 0, dq=bdq, dk=bdk, dv=bdv,
                                         scale=cfg.scale, causal=cfg.causal, workspace=bws, stream=stream)
 
-                for _ in range(2):
-                    backward_drop()
-                e0.record(stream)
-                for _ in range(5):
-                    backward_drop()
-                e1.record(stream)
-                torch.cuda.synchronize()
-                ms_d = e0.elapsed_time(e1) / 5
+                ms_d = settled_ms(lambda i: backward_drop(), 5)
                 detail["bwd_dropout_" + name] = {"us": round(ms_d * 1e3, 2), "TFLOP/s": round(fl / ms_d / 1e9, 1),
                                                  "frac_mfma": round(fl / ms_d / 1e9 / PEAK_BF16_TFLOPS, 4),
                                                  "time_vs_plain": round(ms_d / ms, 3)}
@@ -641,15 +634,7 @@ def main():
             ta.attn_fwd_paged(pq, pkc, pvc, pbt, pcl, out=pout, lse=plse, scale=pcfg.scale, causal=pcfg.causal,
                               stream=stream)
 
-        for _ in range(3):
-            prefill()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(10):
-            prefill()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / 10
+        ms = settled_ms(lambda i: prefill(), 10)
         ctx = pin.ctx_lens.numpy().astype(np.int64)
         i = np.arange(pcfg.Lq)
         pairs = int(sum(np.clip(c - pcfg.Lq + i + 1, 0, c).sum() for c in ctx))
