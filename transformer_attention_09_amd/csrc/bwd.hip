@@ -545,7 +545,7 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256, SPLIT ? 1 : 2) void bwd_dq_kerne
                       (W < 0 || jt >= wr_hi + off - W) && (W < 0 || a.causal || jt + C::BN - 1 <= wr_lo + off + W) &&
                       (wr_lo + 31 < a.Lq);
     uint32_t pw[4][4];
-    // Dropout: bit 16*kh + r keeps register r of half kh; registers 4g'..4g'+3
+    // Dropout: bit keep_bit(16*kh + r) keeps register r of half kh; registers 4g'..4g'+3
     // of half kh are the keys of the 4-key group with counter word 0 =
     // 16*t + 2*(4*kh + g') + hh, and the two rows of a pair sit in lanes l, l^1.
     uint32_t kbits = 0u;
@@ -566,7 +566,7 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256, SPLIT ? 1 : 2) void bwd_dq_kerne
         }
         const float p = fast_exp2(x);
         if constexpr (DROP)
-          sv[r] = p * (((kbits >> (16 * kh + r)) & 1u ? pt[kh][r] * a.drop_scale : 0.f) - dvv);
+          sv[r] = p * (((kbits >> keep_bit(16 * kh + r)) & 1u ? pt[kh][r] * a.drop_scale : 0.f) - dvv);
         else
           sv[r] = p * (pt[kh][r] - dvv);
       }

@@ -30,6 +30,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -363,18 +364,26 @@ __device__ __forceinline__ uint32_t drop_flags2(uint32_t w, uint32_t thr2, uint3
   return d;
 }
 
-// Nibble k of a 16-bit value moved to bits 8k .. 8k+3.
-__device__ __forceinline__ uint32_t spread_nibbles(uint32_t x) {
-  x = ((x << 8) | x) & 0x00FF00FFu;
-  return ((x << 4) | x) & 0x0F0F0F0Fu;
+// Bit of element e (e = 0..31) in a 32-element keep mask in pair order:
+// elements 2m and 2m+1 at bits m and 16 + m, so that one shift and one mask
+// give a packed pair's two decisions as the 16-bit halves of a word.
+__host__ __device__ constexpr int keep_bit(int e) { return (e >> 1) + 16 * (e & 1); }
+
+// 16 decisions x, bit n = 4k + w (k = 0..3, w = 0..3), moved to the pair-order
+// bit of element 8k + w: bit 4k + w/2 for even w, 16 + 4k + (w-1)/2 for odd w.
+__device__ __forceinline__ uint32_t pair_order(uint32_t x) {
+  uint32_t ev = x & 0x5555u, od = (x >> 1) & 0x5555u;
+  ev = (ev | (ev >> 1)) & 0x3333u;
+  od = (od | (od >> 1)) & 0x3333u;
+  return ev | (od << 16);
 }
 
-// Keep bits of one row over eight 4-key groups whose counter words 0 are
-// c0 + 2g (g = 0..7): bit 4g + (key % 4), set = kept.  For layouts with one
-// row per lane in which the other row of the pair (row ^ 1) is in lane ^ 1
-// (and every lane of the wave is active): each lane draws the four calls of
-// the groups g with g % 2 == row % 2 and the two lanes trade the decisions
-// for each other's row.
+// Keep mask of one row over eight 4-key groups whose counter words 0 are
+// c0 + 2g (g = 0..7): element 4g + (key % 4) at bit keep_bit(element), set =
+// kept.  For layouts with one row per lane in which the other row of the pair
+// (row ^ 1) is in lane ^ 1 (and every lane of the wave is active): each lane
+// draws the four calls of the groups g with g % 2 == row % 2 and the two
+// lanes trade the decisions for each other's row.
 __device__ __forceinline__ uint32_t keep_bits_row_pair(uint32_t c0, uint32_t row, uint32_t bh, uint32_t offset,
                                                        uint32_t k0, uint32_t k1, uint32_t thr) {
   const uint32_t par = row & 1u;
@@ -393,8 +402,9 @@ __device__ __forceinline__ uint32_t keep_bits_row_pair(uint32_t c0, uint32_t row
   // low-half flags at bits 16 + n.
   const uint32_t rev = __builtin_bitreverse32(acc);
   const uint32_t lo = rev >> 16, hi = rev & 0xFFFFu;
-  const uint32_t mine = spread_nibbles(par ? hi : lo) << (4u * par);
-  const uint32_t other = spread_nibbles(par ? lo : hi) << (4u * par);
+  // element 4(2k + par) + w: pair-order bit 4k + 2par + ... (pair_order, shifted)
+  const uint32_t mine = pair_order(par ? hi : lo) << (2u * par);
+  const uint32_t other = pair_order(par ? lo : hi) << (2u * par);
   constexpr int kSwapPairs = 1 | (0 << 2) | (3 << 4) | (2 << 6);  // quad_perm [1,0,3,2]
   const uint32_t got = (uint32_t)__builtin_amdgcn_mov_dpp((int)other, kSwapPairs, 0xF, 0xF, false);
   return ~(mine | got);

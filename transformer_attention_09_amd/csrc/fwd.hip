@@ -378,8 +378,8 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256, SPLIT ? 1 : 2) void fwd_kernel(F
     return max_xor32(mx);
   };
 
-  // Dropout decisions of a tile's 32 elements in this lane, bit e for
-  // element e.  Element e is key 8*(e/4) + 4*hh + e%4 of the tile, so the
+  // Dropout decisions of a tile's 32 elements in this lane, element e at
+  // bit keep_bit(e).  Element e is key 8*(e/4) + 4*hh + e%4 of the tile, so the
   // elements 4g..4g+3 are the four words of the call whose counter word 0 is
   // 16*t + 2*g + hh; the two rows of a pair sit in lanes l and l^1.
   // The empty asm statement makes the counter and the key opaque at each
@@ -492,12 +492,11 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256, SPLIT ? 1 : 2) void fwd_kernel(F
       if (e & 1) {
         uint32_t w = pack2<TT>(px[e - 1], px[e]);
         // Dropped probabilities are zeroed in the packed operand only (the
-        // row sum keeps every probability): each keep bit, sign-extended,
-        // masks its 16-bit half.
+        // row sum keeps every probability): the pair's two keep bits (pair
+        // order) multiply its two 16-bit halves.
         if constexpr (DROP) {
-          const uint32_t lo = (uint32_t)__builtin_amdgcn_sbfe((int)kbits, e - 1, 1);
-          const uint32_t hi = (uint32_t)__builtin_amdgcn_sbfe((int)kbits, e, 1);
-          w &= (lo & 0x0000FFFFu) | (hi & 0xFFFF0000u);
+          const uint32_t b = (kbits >> keep_bit(e - 1)) & 0x00010001u;
+          w = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2_t, w) * __builtin_bit_cast(u16x2_t, b));
         }
         pw[e >> 3][(e & 7) >> 1] = w;
       }
