@@ -402,7 +402,9 @@ __device__ __forceinline__ uint32_t keep_bits_row_pair(uint32_t c0, uint32_t row
   // low-half flags at bits 16 + n.
   const uint32_t rev = __builtin_bitreverse32(acc);
   const uint32_t lo = rev >> 16, hi = rev & 0xFFFFu;
-  // element 4(2k + par) + w: pair-order bit 4k + 2par + ... (pair_order, shifted)
+  // This lane drew groups g = 2k + par, so its decisions are elements
+  // e = 8k + 4par + w, whose pair-order bits are those of element 8k + w
+  // (pair_order) moved up by 2par; the other lane's are for groups 2k + 1 - par.
   const uint32_t mine = pair_order(par ? hi : lo) << (2u * par);
   const uint32_t other = pair_order(par ? lo : hi) << (2u * par);
   constexpr int kSwapPairs = 1 | (0 << 2) | (3 << 4) | (2 << 6);  // quad_perm [1,0,3,2]

@@ -46,8 +46,9 @@
 //          longest first when there are at most 64 of them;
 //   DROP   dropout on the probabilities ("dropout_p" of the flash-attn call
 //          on the «Flash Attention» page): each tile's keep decisions come
-//          from Philox4x32-10 at a per-element counter, drawn at the end of
-//          the previous tile; dropped probabilities still enter the row sum;
+//          from Philox4x32-10, one call per four keys of two neighbouring
+//          rows, drawn at the end of the previous tile; dropped
+//          probabilities still enter the row sum;
 //   SPLIT  for grids of at most one work-group per CU (any of the above):
 //          8 waves, two 4-wave halves over alternate key tiles of the same
 //          rows, merged through LDS at the end (two waves per SIMD).
