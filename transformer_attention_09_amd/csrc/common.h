@@ -310,14 +310,20 @@ constexpr float kLn2 = 0.69314718055994530942f;
 __device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
   return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
 }
+// One round with the round's key (k0r, k1r).
+__device__ __forceinline__ void philox_round(uint4& c, uint32_t k0r, uint32_t k1r) {
+  const uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
+  const uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
+  c = make_uint4(xor3((uint32_t)(p1 >> 32), c.y, k0r), (uint32_t)p1, xor3((uint32_t)(p0 >> 32), c.w, k1r), (uint32_t)p0);
+}
+// The Weyl increments of the key after every round.
+constexpr uint32_t kPhiloxW0 = 0x9E3779B9u, kPhiloxW1 = 0xBB67AE85u;
 __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    const uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
-    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
-    c = make_uint4(xor3((uint32_t)(p1 >> 32), c.y, k0), (uint32_t)p1, xor3((uint32_t)(p0 >> 32), c.w, k1), (uint32_t)p0);
-    k0 += 0x9E3779B9u;
-    k1 += 0xBB67AE85u;
+    philox_round(c, k0, k1);
+    k0 += kPhiloxW0;
+    k1 += kPhiloxW1;
   }
   return c;
 }
@@ -383,20 +389,25 @@ __device__ __forceinline__ uint32_t pair_order(uint32_t x) {
 // kept.  For layouts with one row per lane in which the other row of the pair
 // (row ^ 1) is in lane ^ 1 (and every lane of the wave is active): each lane
 // draws the four calls of the groups g with g % 2 == row % 2 and the two
-// lanes trade the decisions for each other's row.
-__device__ __forceinline__ uint32_t keep_bits_row_pair(uint32_t c0, uint32_t row, uint32_t bh, uint32_t offset,
-                                                       uint32_t k0, uint32_t k1, uint32_t thr) {
+// lanes trade the decisions for each other's row.  In steps, so that a caller
+// can spread the calls' rounds over other work:
+//   keep_call(c0, row, bh, offset, k)  counter of this lane's call k (0..3);
+//   keep_fold(acc, r, thr2)            after call k (in order k = 0..3),
+//                                      acc = keep_fold(acc, output, thr2);
+//   keep_finish(acc, row)              the mask from the folded flags.
+__device__ __forceinline__ uint4 keep_call(uint32_t c0, uint32_t row, uint32_t bh, uint32_t offset, int k) {
+  return make_uint4(c0 + 2u * (row & 1u) + 4u * (uint32_t)k, row >> 1, bh, offset);
+}
+__device__ __forceinline__ uint32_t keep_fold(uint32_t acc, uint4 r, uint32_t thr2) {
+  constexpr uint32_t ones2 = 0x00010001u;
+  acc = (acc << 1) | drop_flags2(r.x, thr2, ones2);
+  acc = (acc << 1) | drop_flags2(r.y, thr2, ones2);
+  acc = (acc << 1) | drop_flags2(r.z, thr2, ones2);
+  acc = (acc << 1) | drop_flags2(r.w, thr2, ones2);
+  return acc;
+}
+__device__ __forceinline__ uint32_t keep_finish(uint32_t acc, uint32_t row) {
   const uint32_t par = row & 1u;
-  const uint32_t thr2 = thr | (thr << 16), ones2 = 0x00010001u;
-  uint32_t acc = 0u;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint4 r = philox4x32_10(make_uint4(c0 + 2u * par + 4u * (uint32_t)k, row >> 1, bh, offset), k0, k1);
-    acc = (acc << 1) | drop_flags2(r.x, thr2, ones2);
-    acc = (acc << 1) | drop_flags2(r.y, thr2, ones2);
-    acc = (acc << 1) | drop_flags2(r.z, thr2, ones2);
-    acc = (acc << 1) | drop_flags2(r.w, thr2, ones2);
-  }
   // Word n = 4k + w has its low-half flag at bit 15 - n and its high-half
   // flag at bit 31 - n; reversed, the high-half flags sit at bits n and the
   // low-half flags at bits 16 + n.
@@ -410,6 +421,14 @@ __device__ __forceinline__ uint32_t keep_bits_row_pair(uint32_t c0, uint32_t row
   constexpr int kSwapPairs = 1 | (0 << 2) | (3 << 4) | (2 << 6);  // quad_perm [1,0,3,2]
   const uint32_t got = (uint32_t)__builtin_amdgcn_mov_dpp((int)other, kSwapPairs, 0xF, 0xF, false);
   return ~(mine | got);
+}
+__device__ __forceinline__ uint32_t keep_bits_row_pair(uint32_t c0, uint32_t row, uint32_t bh, uint32_t offset,
+                                                       uint32_t k0, uint32_t k1, uint32_t thr) {
+  const uint32_t thr2 = thr | (thr << 16);
+  uint32_t acc = 0u;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) acc = keep_fold(acc, philox4x32_10(keep_call(c0, row, bh, offset, k), k0, k1), thr2);
+  return keep_finish(acc, row);
 }
 
 // f(std::integral_constant<int, i>) for i = 0..N-1, expanded at compile time,

@@ -47,8 +47,8 @@
 //   DROP   dropout on the probabilities ("dropout_p" of the flash-attn call
 //          on the «Flash Attention» page): each tile's keep decisions come
 //          from Philox4x32-10, one call per four keys of two neighbouring
-//          rows, drawn at the end of the previous tile; dropped
-//          probabilities still enter the row sum;
+//          rows, drawn a round at a time between the previous tile's MFMAs;
+//          dropped probabilities still enter the row sum;
 //   SPLIT  for grids of at most one work-group per CU (any of the above):
 //          8 waves, two 4-wave halves over alternate key tiles of the same
 //          rows, merged through LDS at the end (two waves per SIMD).
@@ -502,6 +502,18 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256, SPLIT ? 1 : 2) void fwd_kernel(F
         pw[e >> 3][(e & 7) >> 1] = w;
       }
     };
+    // Dropout: the next tile's decisions are drawn during this tile's
+    // schedule, one Philox round at a time between the MFMAs (call k's round
+    // r in slot (10k + r) * NSLOT / 40), so the generator's vector work
+    // overlaps the matrix unit instead of running after the schedule.  The
+    // counter, the row and the key are opaque here so that no part of a round
+    // is hoisted out of the key loop (its registers are all in use).
+    uint4 dcall = make_uint4(0u, 0u, 0u, 0u);
+    uint32_t dacc = 0u;
+    uint32_t dc0 = (uint32_t)(16 * (t + TS) + hh), drow = (uint32_t)qi, dbh = drop_bh;
+    uint32_t dk0 = a.seed_lo, dk1 = a.seed_hi;
+    if constexpr (DROP) asm volatile("" : "+v"(dc0), "+v"(drow), "+s"(dbh), "+s"(dk0), "+s"(dk1));
+    const uint32_t dthr2 = a.drop_thr | (a.drop_thr << 16);
     __builtin_amdgcn_sched_barrier(0);
     static_for<NSLOT + 2>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
@@ -557,6 +569,16 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256, SPLIT ? 1 : 2) void fwd_kernel(F
           else mx_a = fmaxf(mx_a, snext[1][r]);
         }
       }
+      if constexpr (DROP) {
+        static_for<40>([&](auto jc) {
+          constexpr int j = decltype(jc)::value, k = j / 10, r = j % 10;
+          if constexpr ((j * NSLOT) / 40 == i) {
+            if constexpr (r == 0) dcall = keep_call(dc0, drow, dbh, a.drop_offset, k);
+            philox_round(dcall, dk0 + (uint32_t)r * kPhiloxW0, dk1 + (uint32_t)r * kPhiloxW1);
+            if constexpr (r == 9) dacc = keep_fold(dacc, dcall, dthr2);
+          }
+        });
+      }
       __builtin_amdgcn_sched_barrier(0);
     });
     const float mnext = max_xor32(fmaxf(mx_a, mx_b));
@@ -569,9 +591,7 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256, SPLIT ? 1 : 2) void fwd_kernel(F
     }
     scur[0] = snext[0];
     scur[1] = snext[1];
-    // The next tile's dropout decisions, while its loads complete (few
-    // registers are live here).
-    if constexpr (DROP) kbits = draw_tile(t + TS);
+    if constexpr (DROP) kbits = keep_finish(dacc, drow);
     wait_vmem();
     __syncthreads();
     __builtin_amdgcn_s_setprio(0);
