@@ -375,15 +375,6 @@ __device__ __forceinline__ uint32_t drop_flags2(uint32_t w, uint32_t thr2, uint3
 // give a packed pair's two decisions as the 16-bit halves of a word.
 __host__ __device__ constexpr int keep_bit(int e) { return (e >> 1) + 16 * (e & 1); }
 
-// 16 decisions x, bit n = 4k + w (k = 0..3, w = 0..3), moved to the pair-order
-// bit of element 8k + w: bit 4k + w/2 for even w, 16 + 4k + (w-1)/2 for odd w.
-__device__ __forceinline__ uint32_t pair_order(uint32_t x) {
-  uint32_t ev = x & 0x5555u, od = (x >> 1) & 0x5555u;
-  ev = (ev | (ev >> 1)) & 0x3333u;
-  od = (od | (od >> 1)) & 0x3333u;
-  return ev | (od << 16);
-}
-
 // Keep mask of one row over eight 4-key groups whose counter words 0 are
 // c0 + 2g (g = 0..7): element 4g + (key % 4) at bit keep_bit(element), set =
 // kept.  For layouts with one row per lane in which the other row of the pair
@@ -391,33 +382,37 @@ __device__ __forceinline__ uint32_t pair_order(uint32_t x) {
 // draws the four calls of the groups g with g % 2 == row % 2 and the two
 // lanes trade the decisions for each other's row.  In steps, so that a caller
 // can spread the calls' rounds over other work:
-//   keep_call(c0, row, bh, offset, k)  counter of this lane's call k (0..3);
-//   keep_fold(acc, r, thr2)            after call k (in order k = 0..3),
-//                                      acc = keep_fold(acc, output, thr2);
-//   keep_finish(acc, row)              the mask from the folded flags.
+//   keep_call(c0, row, bh, offset, k)   counter of this lane's call k (0..3);
+//   keep_fold(acc_e, acc_o, r, thr2, k) folds call k's output r;
+//   keep_finish(acc_e, acc_o, row)      the mask from the folded flags.
+// Folding: word w of call k (keys 4g + w, g = 2k + row % 2) has its two rows'
+// drop flags at bits 0 (even row) and 16 (odd row).  The flag of element
+// e = 4g + w sits at keep_bit(e) = 2g + w/2 for even w and 16 + 2g + (w-1)/2
+// for odd w, so even words are shifted into acc_e by 4k + w/2 and odd words
+// into acc_o by 4k + (w-1)/2; the remaining 2 * (row % 2) is added at the end.
+// Each accumulator then holds the even row's flags in its low half and the
+// odd row's in its high half, and two byte permutes gather this lane's row
+// (low half of acc_e, low half of acc_o moved up) and the other row.
 __device__ __forceinline__ uint4 keep_call(uint32_t c0, uint32_t row, uint32_t bh, uint32_t offset, int k) {
   return make_uint4(c0 + 2u * (row & 1u) + 4u * (uint32_t)k, row >> 1, bh, offset);
 }
-__device__ __forceinline__ uint32_t keep_fold(uint32_t acc, uint4 r, uint32_t thr2) {
+__device__ __forceinline__ void keep_fold(uint32_t& acc_e, uint32_t& acc_o, uint4 r, uint32_t thr2, int k) {
   constexpr uint32_t ones2 = 0x00010001u;
-  acc = (acc << 1) | drop_flags2(r.x, thr2, ones2);
-  acc = (acc << 1) | drop_flags2(r.y, thr2, ones2);
-  acc = (acc << 1) | drop_flags2(r.z, thr2, ones2);
-  acc = (acc << 1) | drop_flags2(r.w, thr2, ones2);
-  return acc;
+  acc_e |= drop_flags2(r.x, thr2, ones2) << (4 * k);
+  acc_o |= drop_flags2(r.y, thr2, ones2) << (4 * k);
+  acc_e |= drop_flags2(r.z, thr2, ones2) << (4 * k + 1);
+  acc_o |= drop_flags2(r.w, thr2, ones2) << (4 * k + 1);
 }
-__device__ __forceinline__ uint32_t keep_finish(uint32_t acc, uint32_t row) {
+__device__ __forceinline__ uint32_t keep_finish(uint32_t acc_e, uint32_t acc_o, uint32_t row) {
   const uint32_t par = row & 1u;
-  // Word n = 4k + w has its low-half flag at bit 15 - n and its high-half
-  // flag at bit 31 - n; reversed, the high-half flags sit at bits n and the
-  // low-half flags at bits 16 + n.
-  const uint32_t rev = __builtin_bitreverse32(acc);
-  const uint32_t lo = rev >> 16, hi = rev & 0xFFFFu;
-  // This lane drew groups g = 2k + par, so its decisions are elements
-  // e = 8k + 4par + w, whose pair-order bits are those of element 8k + w
-  // (pair_order) moved up by 2par; the other lane's are for groups 2k + 1 - par.
-  const uint32_t mine = pair_order(par ? hi : lo) << (2u * par);
-  const uint32_t other = pair_order(par ? lo : hi) << (2u * par);
+  acc_e <<= 2u * par;
+  acc_o <<= 2u * par;
+  // Bytes 0-3 of acc_e and 4-7 of acc_o: this row's half of each, then the
+  // other row's.
+  const uint32_t sel_mine = par ? 0x07060302u : 0x05040100u;
+  const uint32_t sel_other = par ? 0x05040100u : 0x07060302u;
+  const uint32_t mine = __builtin_amdgcn_perm(acc_o, acc_e, sel_mine);
+  const uint32_t other = __builtin_amdgcn_perm(acc_o, acc_e, sel_other);
   constexpr int kSwapPairs = 1 | (0 << 2) | (3 << 4) | (2 << 6);  // quad_perm [1,0,3,2]
   const uint32_t got = (uint32_t)__builtin_amdgcn_mov_dpp((int)other, kSwapPairs, 0xF, 0xF, false);
   return ~(mine | got);
@@ -425,10 +420,10 @@ __device__ __forceinline__ uint32_t keep_finish(uint32_t acc, uint32_t row) {
 __device__ __forceinline__ uint32_t keep_bits_row_pair(uint32_t c0, uint32_t row, uint32_t bh, uint32_t offset,
                                                        uint32_t k0, uint32_t k1, uint32_t thr) {
   const uint32_t thr2 = thr | (thr << 16);
-  uint32_t acc = 0u;
+  uint32_t acc_e = 0u, acc_o = 0u;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) acc = keep_fold(acc, philox4x32_10(keep_call(c0, row, bh, offset, k), k0, k1), thr2);
-  return keep_finish(acc, row);
+  for (int k = 0; k < 4; ++k) keep_fold(acc_e, acc_o, philox4x32_10(keep_call(c0, row, bh, offset, k), k0, k1), thr2, k);
+  return keep_finish(acc_e, acc_o, row);
 }
 
 // f(std::integral_constant<int, i>) for i = 0..N-1, expanded at compile time,

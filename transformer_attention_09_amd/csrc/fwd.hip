@@ -509,7 +509,7 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256, SPLIT ? 1 : 2) void fwd_kernel(F
     // counter, the row and the key are opaque here so that no part of a round
     // is hoisted out of the key loop (its registers are all in use).
     uint4 dcall = make_uint4(0u, 0u, 0u, 0u);
-    uint32_t dacc = 0u;
+    uint32_t dacc_e = 0u, dacc_o = 0u;
     uint32_t dc0 = (uint32_t)(16 * (t + TS) + hh), drow = (uint32_t)qi, dbh = drop_bh;
     uint32_t dk0 = a.seed_lo, dk1 = a.seed_hi;
     if constexpr (DROP) asm volatile("" : "+v"(dc0), "+v"(drow), "+s"(dbh), "+s"(dk0), "+s"(dk1));
@@ -575,7 +575,7 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256, SPLIT ? 1 : 2) void fwd_kernel(F
           if constexpr ((j * NSLOT) / 40 == i) {
             if constexpr (r == 0) dcall = keep_call(dc0, drow, dbh, a.drop_offset, k);
             philox_round(dcall, dk0 + (uint32_t)r * kPhiloxW0, dk1 + (uint32_t)r * kPhiloxW1);
-            if constexpr (r == 9) dacc = keep_fold(dacc, dcall, dthr2);
+            if constexpr (r == 9) keep_fold(dacc_e, dacc_o, dcall, dthr2, k);
           }
         });
       }
@@ -591,7 +591,7 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256, SPLIT ? 1 : 2) void fwd_kernel(F
     }
     scur[0] = snext[0];
     scur[1] = snext[1];
-    if constexpr (DROP) kbits = keep_finish(dacc, drow);
+    if constexpr (DROP) kbits = keep_finish(dacc_e, dacc_o, drow);
     wait_vmem();
     __syncthreads();
     __builtin_amdgcn_s_setprio(0);
