@@ -496,6 +496,9 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256, SPLIT ? 1 : 2) void fwd_kernel(F
         // row sum keeps every probability): the pair's two keep bits (pair
         // order) multiply its two 16-bit halves.
         if constexpr (DROP) {
+          // (opaque first: seen through, the packed conversion was split
+          // into two single conversions and a byte permute)
+          asm("" : "+v"(w));
           const uint32_t b = (kbits >> keep_bit(e - 1)) & 0x00010001u;
           w = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2_t, w) * __builtin_bit_cast(u16x2_t, b));
         }
