@@ -280,6 +280,7 @@ int bwd_common(const void* q, const void* k, const void* v, const void* out, con
   // the forward's threshold and scale (attn_fwd_dropout)
   a.drop_thr = drop ? (uint32_t)std::floor((double)dropout_p * 65536.0) : 0u;
   a.drop_scale = drop ? (float)(1.0 / (1.0 - (double)dropout_p)) : 1.f;
+  a.d_mult = drop ? (float)(1.0 - (double)dropout_p) : 1.f;
   a.seed_lo = (uint32_t)seed;
   a.seed_hi = (uint32_t)(seed >> 32);
   a.drop_offset = offset;

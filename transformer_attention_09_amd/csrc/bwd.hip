@@ -31,7 +31,11 @@
 //
 // With dropout (the DROP instances) the forward computed O = (P * M) V with
 // M = keep / (1 - p); then dV = (P * M)^T dO and dS = P * (M * dP - D), where
-// D_i = sum_d dO_id O_id still equals sum_j P_ij M_ij dP_ij.  Both kernels
+// D_i = sum_d dO_id O_id still equals sum_j P_ij M_ij dP_ij.  The factor
+// 1/(1 - p) comes out of all three gradients: the kernels use the 0/1 keep
+// factor K, dV' = (P * K)^T dO and dS' = P * (K * dP - (1 - p) D) (the
+// preprocess stores D (1 - p)), and scale dQ, dK and dV by 1/(1 - p) once,
+// when they are stored.  Both kernels
 // recompute the keep decisions with the forward's Philox counter
 // (j/4, i/2, b*Hq + h, offset): one call gives the four keys 4c..4c+3 of the
 // rows 2m (low 16 bits of each word) and 2m+1 (high 16 bits).  The dQ kernel
@@ -91,7 +95,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
   if (row < nrows && c == 0) {
     const long long h = row % a.Hq, bi = row / a.Hq, i = bi % a.Lq, b = bi / a.Lq;
     const size_t o = ((size_t)b * a.Hq + h) * a.Lq + i;
-    a.Dv[o] = acc;
+    a.Dv[o] = acc * a.d_mult;
     const float l = a.lse[o];
     a.L2[o] = l == -INFINITY ? INFINITY : l * kLog2e;
   }
@@ -299,9 +303,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
             const float lv = e < 4 ? lA[e] : lB[e - 4], dv = e < 4 ? dA[e] : dB[e - 4];
             pv[e] = fast_exp2(__builtin_fmaf(sacc[r], sl2, -lv));
             if constexpr (DROP) {
-              const bool kp = (kbits >> r) & 1u;
-              sv[e] = pv[e] * ((kp ? pacc[r] * a.drop_scale : 0.f) - dv);
-              pv[e] = kp ? pv[e] * a.drop_scale : 0.f;
+              const float kf = (float)((kbits >> r) & 1u);
+              sv[e] = pv[e] * __builtin_fmaf(kf, pacc[r], -dv);
+              pv[e] *= kf;
             } else {
               sv[e] = pv[e] * (pacc[r] - dv);
             }
@@ -319,9 +323,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
             const float x = __builtin_fmaf(sacc[r], sl2, -lv);
             pv[e] = fast_exp2(vis ? x : -INFINITY);
             if constexpr (DROP) {
-              const bool kp = (kbits >> r) & 1u;
-              sv[e] = pv[e] * ((kp ? pacc[r] * a.drop_scale : 0.f) - dv);
-              pv[e] = kp ? pv[e] * a.drop_scale : 0.f;
+              const float kf = (float)((kbits >> r) & 1u);
+              sv[e] = pv[e] * __builtin_fmaf(kf, pacc[r], -dv);
+              pv[e] *= kf;
             } else {
               sv[e] = pv[e] * (pacc[r] - dv);
             }
@@ -394,8 +398,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
       }
       const size_t ro = (((size_t)b * a.Lk + kw0 + l32) * a.Hkv + g) * D;
       const bool key_ok = kw0 + l32 < a.Lk;
-      store_row16<TT, C::DT>((E*)a.dk + ro, dkacc, a.scale, hh, key_ok);
-      store_row16<TT, C::DT>((E*)a.dv + ro, dvacc, 1.f, hh, key_ok);
+      store_row16<TT, C::DT>((E*)a.dk + ro, dkacc, DROP ? a.scale * a.drop_scale : a.scale, hh, key_ok);
+      store_row16<TT, C::DT>((E*)a.dv + ro, dvacc, DROP ? a.drop_scale : 1.f, hh, key_ok);
     }
   }
 }
@@ -566,7 +570,7 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256, SPLIT ? 1 : 2) void bwd_dq_kerne
         }
         const float p = fast_exp2(x);
         if constexpr (DROP)
-          sv[r] = p * (((kbits >> keep_bit(16 * kh + r)) & 1u ? pt[kh][r] * a.drop_scale : 0.f) - dvv);
+          sv[r] = p * __builtin_fmaf((float)((kbits >> keep_bit(16 * kh + r)) & 1u), pt[kh][r], -dvv);
         else
           sv[r] = p * (pt[kh][r] - dvv);
       }
@@ -626,13 +630,14 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256, SPLIT ? 1 : 2) void bwd_dq_kerne
     // The dropout instance has no registers to spare for the lane-pair swap
     // of store_row16 (its D = 128 kernel would spill): 8-byte stores.
     if (qi < a.Lq) {
+      const float sc = a.scale * a.drop_scale;
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
           *(uint2*)(dqrow + 32 * dt + 8 * q4 + 4 * hh) =
-              make_uint2(pack2<TT>(dqacc[dt][4 * q4] * a.scale, dqacc[dt][4 * q4 + 1] * a.scale),
-                         pack2<TT>(dqacc[dt][4 * q4 + 2] * a.scale, dqacc[dt][4 * q4 + 3] * a.scale));
+              make_uint2(pack2<TT>(dqacc[dt][4 * q4] * sc, dqacc[dt][4 * q4 + 1] * sc),
+                         pack2<TT>(dqacc[dt][4 * q4 + 2] * sc, dqacc[dt][4 * q4 + 3] * sc));
     }
   } else {
     store_row16<TT, C::DT>(dqrow, dqacc, a.scale, hh, qi < a.Lq);

@@ -82,9 +82,13 @@ struct BwdArgs {
   float scale_log2;
   int n_qblocks;
   // Dropout (attn_bwd_dropout): the forward's keep decisions, recomputed
-  // with the same Philox counter, key and threshold as FwdArgs.
+  // with the same Philox counter, key and threshold as FwdArgs.  The kernels
+  // accumulate with 0/1 keep factors and D * (1 - p) (d_mult = 1 - p; 1
+  // without dropout), and multiply dQ, dK and dV by drop_scale = 1/(1-p)
+  // once when they store them.
   uint32_t drop_thr, seed_lo, seed_hi, drop_offset;
   float drop_scale;
+  float d_mult;
   // The dQ kernel splits each work-group's key tiles between two 4-wave
   // halves (set when its grid has no more work-groups than the device has CUs).
   int kv_split;
