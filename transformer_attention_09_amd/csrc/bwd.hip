@@ -257,34 +257,52 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
       // lane q of a quad draws the pairs of registers 8s + 2q (s = 0, 1), and
       // the transpose hands each lane its key's word of the four lanes' calls,
       // so the word of lane c in round s holds registers 8s + 2c (low half)
-      // and 8s + 2c + 1 (high half).  Drawn before the products, while few
-      // registers are live.
+      // and 8s + 2c + 1 (high half).  The two calls' twenty rounds run between
+      // the S and dP products (round j after the products of k-step
+      // j * DSTEPS / 20), one call in flight, so the generator's vector work
+      // overlaps the matrix unit.
       uint32_t kbits = 0u;
+      f32x16 sacc = f32x16{}, pacc = f32x16{};
       if constexpr (DROP) {
         const uint32_t thr2 = a.drop_thr | (a.drop_thr << 16);
+        const int q = l32 & 3;
         uint32_t drop = 0u;
+        uint4 dc = make_uint4(0u, 0u, 0u, 0u);
+        uint32_t c0 = (uint32_t)(key >> 2), rowq = (uint32_t)(i0 + rb * 32 + 4 * hh + 8 * (q >> 1) + 2 * (q & 1));
+        uint32_t k0 = a.seed_lo, k1 = a.seed_hi, dbh = drop_bh;
+        asm volatile("" : "+v"(rowq), "+v"(c0), "+s"(k0), "+s"(k1), "+s"(dbh));
+        static_for<C::DSTEPS>([&](auto sc) {
+          constexpr int s = decltype(sc)::value;
+          sacc = TT::mfma32(*(const V8*)(qs + noff[s] + rb * 32 * D), *(const V8*)(kblk + koff + noff[s]), sacc);
+          pacc = TT::mfma32(*(const V8*)(gs + noff[s] + rb * 32 * D), *(const V8*)(vblk + koff + noff[s]), pacc);
+          static_for<20>([&](auto jc) {
+            constexpr int j = decltype(jc)::value, s2 = j / 10, r = j % 10;
+            if constexpr ((j * C::DSTEPS) / 20 == s) {
+              if constexpr (r == 0) {
+                const uint32_t row = rowq + 16u * s2;
+                dc = make_uint4(c0, row >> 1, dbh, a.drop_offset);
+              }
+              philox_round(dc, k0 + (uint32_t)r * kPhiloxW0, k1 + (uint32_t)r * kPhiloxW1);
+              if constexpr (r == 9) {
+                uint32_t w[4] = {dc.x, dc.y, dc.z, dc.w};
+                quad_transpose(w, q);
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const int q = l32 & 3;
-          uint32_t row = (uint32_t)(i0 + rb * 32 + 4 * hh + 8 * ((q >> 1) + 2 * s2) + 2 * (q & 1));
-          uint32_t c0 = (uint32_t)(key >> 2), k0 = a.seed_lo, k1 = a.seed_hi;
-          asm volatile("" : "+v"(row), "+v"(c0), "+s"(k0), "+s"(k1));
-          const uint4 r = philox4x32_10(make_uint4(c0, row >> 1, drop_bh, a.drop_offset), k0, k1);
-          uint32_t w[4] = {r.x, r.y, r.z, r.w};
-          quad_transpose(w, q);
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const uint32_t f = drop_flags2(w[c], thr2, 0x00010001u);
-            drop |= ((f & 1u) | ((f >> 15) & 2u)) << (8 * s2 + 2 * c);
-          }
-        }
+                for (int c = 0; c < 4; ++c) {
+                  const uint32_t f = drop_flags2(w[c], thr2, 0x00010001u);
+                  drop |= ((f & 1u) | ((f >> 15) & 2u)) << (8 * s2 + 2 * c);
+                }
+              }
+            }
+          });
+          __builtin_amdgcn_sched_barrier(0);
+        });
         kbits = ~drop & 0xFFFFu;
-      }
-      f32x16 sacc = f32x16{}, pacc = f32x16{};
+      } else {
 #pragma unroll
-      for (int s = 0; s < C::DSTEPS; ++s) {
-        sacc = TT::mfma32(*(const V8*)(qs + noff[s] + rb * 32 * D), *(const V8*)(kblk + koff + noff[s]), sacc);
-        pacc = TT::mfma32(*(const V8*)(gs + noff[s] + rb * 32 * D), *(const V8*)(vblk + koff + noff[s]), pacc);
+        for (int s = 0; s < C::DSTEPS; ++s) {
+          sacc = TT::mfma32(*(const V8*)(qs + noff[s] + rb * 32 * D), *(const V8*)(kblk + koff + noff[s]), sacc);
+          pacc = TT::mfma32(*(const V8*)(gs + noff[s] + rb * 32 * D), *(const V8*)(vblk + koff + noff[s]), pacc);
+        }
       }
       // Two row steps of 16 (registers 8*h2 .. 8*h2+7): their P and dS, packed
       // to the input type, then the step's dV and dK products.
@@ -535,12 +553,45 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256, SPLIT ? 1 : 2) void bwd_dq_kerne
       st[kh] = f32x16{};
       pt[kh] = f32x16{};
     }
+    // Dropout: bit keep_bit(16*kh + r) keeps register r of half kh; registers 4g'..4g'+3
+    // of half kh are the keys of the 4-key group with counter word 0 =
+    // 16*t + 2*(4*kh + g') + hh, and the two rows of a pair sit in lanes l, l^1.
+    // The four calls' forty rounds run between the products (round j after
+    // k-step j * DSTEPS / 40), one call in flight, so the generator's vector
+    // work overlaps the matrix unit.
+    uint32_t kbits = 0u;
+    if constexpr (DROP) {
+      uint32_t c0 = (uint32_t)(16 * t + hh), row = (uint32_t)qi, k0 = a.seed_lo, k1 = a.seed_hi, dbh = drop_bh;
+      asm volatile("" : "+v"(c0), "+v"(row), "+s"(k0), "+s"(k1), "+s"(dbh));
+      const uint32_t thr2 = a.drop_thr | (a.drop_thr << 16);
+      uint4 dc = make_uint4(0u, 0u, 0u, 0u);
+      uint32_t acc_e = 0u, acc_o = 0u;
+      static_for<C::DSTEPS>([&](auto sc) {
+        constexpr int s = decltype(sc)::value;
 #pragma unroll
-    for (int s = 0; s < C::DSTEPS; ++s) {
+        for (int kh = 0; kh < 2; ++kh) {
+          st[kh] = TT::mfma32(*(const V8*)(ks + noff[s] + kh * 32 * D), qf[s], st[kh]);
+          pt[kh] = TT::mfma32(*(const V8*)(vs + noff[s] + kh * 32 * D), gf[s], pt[kh]);
+        }
+        static_for<40>([&](auto jc) {
+          constexpr int j = decltype(jc)::value, k = j / 10, r = j % 10;
+          if constexpr ((j * C::DSTEPS) / 40 == s) {
+            if constexpr (r == 0) dc = keep_call(c0, row, dbh, a.drop_offset, k);
+            philox_round(dc, k0 + (uint32_t)r * kPhiloxW0, k1 + (uint32_t)r * kPhiloxW1);
+            if constexpr (r == 9) keep_fold(acc_e, acc_o, dc, thr2, k);
+          }
+        });
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      kbits = keep_finish(acc_e, acc_o, row);
+    } else {
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-        st[kh] = TT::mfma32(*(const V8*)(ks + noff[s] + kh * 32 * D), qf[s], st[kh]);
-        pt[kh] = TT::mfma32(*(const V8*)(vs + noff[s] + kh * 32 * D), gf[s], pt[kh]);
+      for (int s = 0; s < C::DSTEPS; ++s) {
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+          st[kh] = TT::mfma32(*(const V8*)(ks + noff[s] + kh * 32 * D), qf[s], st[kh]);
+          pt[kh] = TT::mfma32(*(const V8*)(vs + noff[s] + kh * 32 * D), gf[s], pt[kh]);
+        }
       }
     }
     // Register r of half kh is key t*BN + kh*32 + 8*(r/4) + 4*hh + r%4.
@@ -549,15 +600,6 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256, SPLIT ? 1 : 2) void bwd_dq_kerne
                       (W < 0 || jt >= wr_hi + off - W) && (W < 0 || a.causal || jt + C::BN - 1 <= wr_lo + off + W) &&
                       (wr_lo + 31 < a.Lq);
     uint32_t pw[4][4];
-    // Dropout: bit keep_bit(16*kh + r) keeps register r of half kh; registers 4g'..4g'+3
-    // of half kh are the keys of the 4-key group with counter word 0 =
-    // 16*t + 2*(4*kh + g') + hh, and the two rows of a pair sit in lanes l, l^1.
-    uint32_t kbits = 0u;
-    if constexpr (DROP) {
-      uint32_t c0 = (uint32_t)(16 * t + hh), row = (uint32_t)qi, k0 = a.seed_lo, k1 = a.seed_hi;
-      asm volatile("" : "+v"(c0), "+v"(row), "+s"(k0), "+s"(k1));
-      kbits = keep_bits_row_pair(c0, row, drop_bh, a.drop_offset, k0, k1, a.drop_thr);
-    }
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
       float sv[16];
