@@ -264,6 +264,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
       uint32_t kbits = 0u;
       f32x16 sacc = f32x16{}, pacc = f32x16{};
       if constexpr (DROP) {
+        // The S and dP products read their operands (Q, K, dO and V rows) one
+        // k-step ahead, into alternating registers, so that the reads overlap
+        // the previous step's products and the draws.
+        V8 op[2][4];
+        auto read_op = [&](int s, V8 (&o)[4]) {
+          o[0] = *(const V8*)(qs + noff[s] + rb * 32 * D);
+          o[1] = *(const V8*)(kblk + koff + noff[s]);
+          o[2] = *(const V8*)(gs + noff[s] + rb * 32 * D);
+          o[3] = *(const V8*)(vblk + koff + noff[s]);
+        };
         const uint32_t thr2 = a.drop_thr | (a.drop_thr << 16);
         const int q = l32 & 3;
         uint32_t drop = 0u;
@@ -271,10 +281,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
         uint32_t c0 = (uint32_t)(key >> 2), rowq = (uint32_t)(i0 + rb * 32 + 4 * hh + 8 * (q >> 1) + 2 * (q & 1));
         uint32_t k0 = a.seed_lo, k1 = a.seed_hi, dbh = drop_bh;
         asm volatile("" : "+v"(rowq), "+v"(c0), "+s"(k0), "+s"(k1), "+s"(dbh));
+        read_op(0, op[0]);
         static_for<C::DSTEPS>([&](auto sc) {
           constexpr int s = decltype(sc)::value;
-          sacc = TT::mfma32(*(const V8*)(qs + noff[s] + rb * 32 * D), *(const V8*)(kblk + koff + noff[s]), sacc);
-          pacc = TT::mfma32(*(const V8*)(gs + noff[s] + rb * 32 * D), *(const V8*)(vblk + koff + noff[s]), pacc);
+          if constexpr (s + 1 < C::DSTEPS) read_op(s + 1, op[(s + 1) & 1]);
+          __builtin_amdgcn_sched_barrier(0);
+          sacc = TT::mfma32(op[s & 1][0], op[s & 1][1], sacc);
+          pacc = TT::mfma32(op[s & 1][2], op[s & 1][3], pacc);
           static_for<20>([&](auto jc) {
             constexpr int j = decltype(jc)::value, s2 = j / 10, r = j % 10;
             if constexpr ((j * C::DSTEPS) / 20 == s) {
