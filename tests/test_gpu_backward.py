@@ -113,6 +113,29 @@ def test_backward_workloads(gpu_lib, name):
     check_grads(f"backward {name}", got, ref, cfg.dtype)
 
 
+@pytest.mark.parametrize("name", ["gqa8k_causal", "gqa8k_window"])
+def test_backward_long_gqa_two_kv_heads_in_full(gpu_lib, name):
+    """The long GQA backward at its full size (B1 Hq32 Hkv8 L8192 D128 bf16,
+    causal, and with the 4096-key window), every head run on the GPU in the
+    launch configuration the bench times.  Heads are independent, so the
+    oracle differentiates the first and the last KV head with their query
+    heads (8 of the 32, about 20 s of CPU) and every element of their dQ, dK
+    and dV is compared: all rows and all keys."""
+    cfg = CONFIGS[name]
+    say(f"[case] backward workload {name} (KV heads 0 and {cfg.Hkv - 1} in full)")
+    q, k, v = dense_inputs(cfg)
+    do = _dout(q.shape, cfg.dtype, 701)
+    dq, dk, dv = run_bwd(gpu_lib, q, k, v, do, cfg.scale, cfg.causal, cfg.window)
+    group = cfg.Hq // cfg.Hkv
+    gs = [0, cfg.Hkv - 1]
+    hs = [h for h in range(cfg.Hq) if h // group in gs]
+    got = (dq[:, :, hs].cpu(), dk[:, :, gs].cpu(), dv[:, :, gs].cpu())
+    del dq, dk, dv
+    ref = oracle.attention_backward(q[:, :, hs], k[:, :, gs], v[:, :, gs], do[:, :, hs], cfg.scale, cfg.causal,
+                                    cfg.window)
+    check_grads(f"backward {name} (KV heads {gs})", got, ref, cfg.dtype)
+
+
 def test_backward_deterministic_bitwise(gpu_lib):
     q, k, v = random_dense(2, 8, 2, 300, 300, 128, "bf16", 801)
     do = _dout(q.shape, "bf16", 802)
