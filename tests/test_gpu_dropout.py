@@ -305,6 +305,29 @@ def test_dropout_backward_workload_std2048(gpu_lib):
         assert err <= tol
 
 
+def test_dropout_backward_long_gqa_first_kv_head_in_full(gpu_lib):
+    """The long causal GQA backward with dropout (p = 0.1) at its full size
+    (B1 Hq32 Hkv8 L8192 D128 bf16), every head run on the GPU.  With B = 1
+    the first KV head's four query heads are heads 0..3 of the problem, so the
+    oracle on that slice draws the same keep decisions (counter word 2 is
+    b*Hq + h); every element of their dQ and of KV head 0's dK and dV is
+    compared (about 30 s and 6 GB of CPU)."""
+    cfg = CONFIGS["gqa8k_causal"]
+    say("[case] dropout bwd workload gqa8k_causal p0.1 (KV head 0 in full)")
+    q, k, v = dense_inputs(cfg)
+    do = _dout(q.shape, cfg.dtype, 1801)
+    dq, dk, dv = run_bwd_drop(gpu_lib, q, k, v, do, 0.1, 1234, 3, cfg.scale, cfg.causal, cfg.window)
+    hs = list(range(cfg.Hq // cfg.Hkv))
+    got = (dq[:, :, hs], dk[:, :, :1], dv[:, :, :1])
+    ref = oracle.attention_dropout_backward(q[:, :, hs], k[:, :, :1], v[:, :, :1], do[:, :, hs], cfg.scale,
+                                            cfg.causal, cfg.window, 0.1, 1234, 3)
+    for n, g, r in zip(("dq", "dk", "dv"), got, ref):
+        err = float(np.max(np.abs(g.double().cpu().numpy() - r)))
+        tol = GTOL[cfg.dtype] * max(1.0, float(np.max(np.abs(r)))) / 0.9
+        say(f"  {n} max-abs {err:.3e} (tol {tol:.2e})")
+        assert err <= tol
+
+
 def _rand_drop_cases(n=12):
     r = np.random.default_rng(8642)
     out = []
