@@ -144,6 +144,20 @@ def test_dropout_workloads_sampled_rows(gpu_lib, name, p):
     check_out(name, out, lse, q, k, v, cfg.scale, cfg.causal, cfg.window, p, 77, 1, cfg.dtype, rows=rows)
 
 
+def test_dropout_long_gqa_first_kv_head_all_rows(gpu_lib):
+    """The long causal GQA forward with dropout (p = 0.1) at its full size,
+    every head run on the GPU; with B = 1 the first KV head's query heads are
+    heads 0..3 of the problem, so the oracle on that slice draws the same keep
+    decisions, and every output row of those heads is compared."""
+    cfg = CONFIGS["gqa8k_causal"]
+    say("[case] dropout workload gqa8k_causal p0.1 (KV head 0, all rows)")
+    q, k, v = dense_inputs(cfg)
+    out, lse = run_drop(gpu_lib, q, k, v, 0.1, 77, 1, cfg.scale, cfg.causal, cfg.window)
+    hs = list(range(cfg.Hq // cfg.Hkv))
+    check_out("gqa8k_causal dropout KV head 0", out[:, :, hs], lse[:, hs], q[:, :, hs], k[:, :, :1], v[:, :, :1],
+              cfg.scale, cfg.causal, cfg.window, 0.1, 77, 1, cfg.dtype)
+
+
 def test_dropout_deterministic_and_offset_changes_mask(gpu_lib):
     q, k, v = (t.to("cuda") for t in random_dense(1, 4, 2, 300, 300, 128, "bf16", 1300))
     a = gpu_lib.attn_fwd_dropout(q, k, v, 0.3, 11, 0, causal=True)

@@ -101,6 +101,22 @@ def test_fp8_workloads_sampled_rows(gpu_lib, name):
     check_fp8(name, out, lse, q, k, v, cfg.scale, cfg.causal, cfg.window, rows=rows)
 
 
+@pytest.mark.parametrize("name", ["fp8_causal", "gqa8k_causal_fp8"])
+def test_fp8_workloads_first_and_last_kv_head_all_rows(gpu_lib, name):
+    """The FP8 workloads at full size, every head run on the GPU; heads are
+    independent, so the query heads of the first and the last KV head are
+    compared with the oracle on every row."""
+    cfg = CONFIGS[name]
+    q, k, v = dense_inputs(cfg)
+    out, lse = run_fp8(gpu_lib, q, k, v, cfg.scale, cfg.causal, cfg.window)
+    group = cfg.Hq // cfg.Hkv
+    gs = [0, cfg.Hkv - 1]
+    hs = [h for h in range(cfg.Hq) if h // group in gs]
+    say(f"[case] fp8 workload {name} (KV heads {gs}, all rows)")
+    check_fp8(f"{name} KV heads {gs}", out[:, :, hs], lse[:, hs], q[:, :, hs], k[:, :, gs], v[:, :, gs], cfg.scale,
+              cfg.causal, cfg.window)
+
+
 def test_fp8_deterministic_bitwise(gpu_lib):
     cfg = DenseConfig("fp8_det", 1, 8, 2, 300, 300, 128, "fp8", True, -1, 960)
     q, k, v = dense_inputs(cfg)
